@@ -1,0 +1,67 @@
+"""Per-row symmetric int8 quantization, int8 x int8 -> int32 matmul, W8A8.
+
+Test infrastructure only (see the package docstring).
+
+Source: "cider/ops.py".
+  * ``quantize_weight_int8`` (absmax branch): cast to fp32,
+    ``scale = rowmax|w| / 127``, a zero scale becomes 1.0,
+    ``q = clip(round(w / scale), -128, 127)`` as int8, scale fp32 ``[N]``.
+  * ``perchannel_linear``: ``y = dequant(quant_a(x) @ w_int8) + bias`` with x
+    ``[M, K]`` fp16/bf16, w int8 ``[N, K]``, ``scale_w`` fp32 ``[N]``, output in
+    the input dtype.
+  * ``int8_matmul_int32``: int8 ``a [M, K]`` times int8 ``b [N, K]`` (the
+    transposed weight layout) to int32 ``[M, N]``, bit-exact.
+
+Reading: the pages name the activation quantizer ``quant_a`` without defining
+it; it is taken to be the same per-row symmetric absmax/127 rule as the weight
+quantizer, applied to each row of x.  The W8A8 reference output is the product
+of the dequantized operands, ``acc * sx[m] * sw[n] (+ bias)``, not x W^T on the
+unquantized values.
+"""
+
+import numpy as np
+
+
+def quantize_rows_int8(v):
+    """Per-row symmetric int8 quantization of ``[R, K]`` values (fp32 steps).
+
+    Returns ``(q int8 [R, K], scale f32 [R])``.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    if v.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    if not np.isfinite(v).all():
+        raise ValueError("non-finite value")
+    a = np.abs(v).max(axis=1) if v.shape[1] else np.zeros(v.shape[0], np.float32)
+    s = (a / np.float32(127.0)).astype(np.float32)
+    s = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+    q = np.clip(np.rint(v / s[:, None]), -128, 127).astype(np.int8)
+    return q, s
+
+
+def int8_matmul_int32(a, b):
+    """Exact ``a [M, K] @ b [N, K]^T`` in int64 (equals int32 when it fits)."""
+    a = np.asarray(a, dtype=np.int8).astype(np.int64)
+    b = np.asarray(b, dtype=np.int8).astype(np.int64)
+    return a @ b.T
+
+
+def w8a8_forward(x, wq, sw, bias=None):
+    """W8A8 per-channel linear in the dequantized-operand reading.
+
+    ``x`` ``[M, K]`` holds the stored fp16/bf16 input values, ``wq`` int8
+    ``[N, K]``, ``sw`` fp32 ``[N]``.  Returns
+    ``(xq int8 [M, K], sx f32 [M], acc int64 [M, N], y_ref fp64 [M, N], D)``
+    with ``y_ref = acc * sx[m] * sw[n] (+ bias[n])`` and
+    ``D = sum_k |xq sx| |wq sw|``.
+    """
+    xq, sx = quantize_rows_int8(x)
+    acc = int8_matmul_int32(xq, wq)
+    sx64 = sx.astype(np.float64)[:, None]
+    sw64 = np.asarray(sw, dtype=np.float32).astype(np.float64)[None, :]
+    y = acc.astype(np.float64) * sx64 * sw64
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    absacc = np.abs(xq.astype(np.int64)) @ np.abs(np.asarray(wq, dtype=np.int64)).T
+    D = absacc.astype(np.float64) * sx64 * np.abs(sw64)
+    return xq, sx, acc, y, D
