@@ -1,0 +1,322 @@
+// C ABI of libqlq: argument validation, device check, dispatch, launches.
+// Every entry point validates on the host before its first HIP call, so an
+// invalid call returns an error without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/qlq.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+int g_skinny_max_m = 8;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+int ok() {
+  g_err.clear();
+  return QLQ_OK;
+}
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool dtype_ok(int d) { return d == QLQ_F32 || d == QLQ_F16 || d == QLQ_BF16; }
+size_t dtype_size(int d) { return d == QLQ_F32 ? 4 : 2; }
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QLQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// gfx950 check, cached per device.
+std::mutex g_dev_mu;
+signed char g_dev_state[64];  // 0 unknown, 1 gfx950, -1 other
+
+int device_status(int dev) {
+  if (dev < 0 || dev >= 64) return fail(QLQ_ERR_DEVICE, "device %d out of range", dev);
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_state[dev] == 1) return QLQ_OK;
+    if (g_dev_state[dev] == -1) return fail(QLQ_ERR_DEVICE, "device %d is not a gfx950", dev);
+  }
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || dev >= count)
+    return fail(QLQ_ERR_DEVICE, "no HIP device %d", dev);
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(QLQ_ERR_DEVICE, "cannot query HIP device %d", dev);
+  const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    g_dev_state[dev] = is950 ? 1 : -1;
+  }
+  if (!is950) return fail(QLQ_ERR_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  return QLQ_OK;
+}
+
+int current_device_status() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(QLQ_ERR_DEVICE, "no current HIP device");
+  }
+  return device_status(dev);
+}
+
+#define QLQ_REQUIRE(cond, code, ...) \
+  do {                               \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+int check_affine_shape(int64_t N, int64_t K, int bits, int G) {
+  QLQ_REQUIRE(N >= 1 && K >= 1 && N < kMaxDim && K < kMaxDim, QLQ_ERR_INVALID_ARG,
+              "invalid shape N=%lld K=%lld", (long long)N, (long long)K);
+  QLQ_REQUIRE(bits == 2 || bits == 4 || bits == 8, QLQ_ERR_UNSUPPORTED, "bits=%d not built (2, 4, 8)", bits);
+  QLQ_REQUIRE(G == 32 || G == 64 || G == 128, QLQ_ERR_UNSUPPORTED,
+              "group_size=%d not built (32, 64, 128)", G);
+  QLQ_REQUIRE(K % G == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of group_size=%d", (long long)K, G);
+  return QLQ_OK;
+}
+
+// The GEMM path takes 16-bit x with K a multiple of its 64-wide k-iteration.
+bool takes_gemm(int64_t M, int64_t K, int x_dtype) {
+  return x_dtype != QLQ_F32 && M > g_skinny_max_m && K % 64 == 0;
+}
+
+// one-shot device int flag for the synchronising pack calls
+struct DevFlag {
+  int* p = nullptr;
+  ~DevFlag() {
+    if (p) (void)hipFree(p);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+QLQ_API const char* qlq_last_error(void) { return g_err.c_str(); }
+QLQ_API const char* qlq_version(void) { return "qlq 0.1.0 (gfx950)"; }
+
+QLQ_API int qlq_device_check(int device) {
+  const int st = device_status(device);
+  return st == QLQ_OK ? ok() : st;
+}
+
+QLQ_API int qlq_set_skinny_max_m(int m) {
+  QLQ_REQUIRE(m >= 0, QLQ_ERR_INVALID_ARG, "skinny max M must be >= 0 (got %d)", m);
+  g_skinny_max_m = m;
+  return ok();
+}
+QLQ_API int qlq_get_skinny_max_m(void) { return g_skinny_max_m; }
+
+// ----------------------------------------------------------------- affine
+QLQ_API int qlq_pack(const float* w, int64_t N, int64_t K, int bits, int group_size, uint32_t* packed,
+                     void* scales, void* biases, int sb_dtype, void* stream) {
+  QLQ_REQUIRE(w && packed && scales && biases, QLQ_ERR_INVALID_ARG, "null pointer");
+  if (int st = check_affine_shape(N, K, bits, group_size)) return st;
+  QLQ_REQUIRE(dtype_ok(sb_dtype), QLQ_ERR_UNSUPPORTED, "sb_dtype %d", sb_dtype);
+  QLQ_REQUIRE(aligned(w, 16), QLQ_ERR_ALIGNMENT, "w not 16-byte aligned");
+  QLQ_REQUIRE(aligned(packed, 4) && aligned(scales, dtype_size(sb_dtype)) &&
+                  aligned(biases, dtype_size(sb_dtype)),
+              QLQ_ERR_ALIGNMENT, "misaligned output");
+  if (int st = current_device_status()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  DevFlag flag;
+  if (int st = hip_status(hipMalloc((void**)&flag.p, sizeof(int)), "hipMalloc(flag)")) return st;
+  if (int st = hip_status(hipMemsetAsync(flag.p, 0, sizeof(int), s), "hipMemsetAsync")) return st;
+  if (int st = hip_status(qlq::launch_affine_pack(w, N, K, bits, group_size, packed, scales, biases,
+                                                  sb_dtype, flag.p, s),
+                          "affine_pack launch"))
+    return st;
+  int host_flag = 0;
+  if (int st = hip_status(hipMemcpyAsync(&host_flag, flag.p, sizeof(int), hipMemcpyDeviceToHost, s),
+                          "hipMemcpyAsync(flag)"))
+    return st;
+  if (int st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize")) return st;
+  QLQ_REQUIRE(host_flag == 0, QLQ_ERR_DATA, "non-finite weight, or scale/bias overflows the storage dtype");
+  return ok();
+}
+
+QLQ_API int qlq_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits, uint8_t* codes,
+                       void* stream) {
+  QLQ_REQUIRE(packed && codes, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(N >= 1 && K >= 1 && N < kMaxDim && K < kMaxDim, QLQ_ERR_INVALID_ARG, "invalid shape");
+  QLQ_REQUIRE(bits == 2 || bits == 4 || bits == 8, QLQ_ERR_UNSUPPORTED, "bits=%d", bits);
+  QLQ_REQUIRE(K % (32 / bits) == 0, QLQ_ERR_INVALID_ARG, "K must fill whole words");
+  QLQ_REQUIRE(aligned(packed, 4), QLQ_ERR_ALIGNMENT, "packed not 4-byte aligned");
+  if (int st = current_device_status()) return st;
+  return hip_status(qlq::launch_affine_unpack(packed, N, K, bits, codes, (hipStream_t)stream), "unpack");
+}
+
+QLQ_API int qlq_dequantize(const uint32_t* packed, const void* scales, const void* biases, int sb_dtype,
+                           int64_t N, int64_t K, int bits, int group_size, float* w, void* stream) {
+  QLQ_REQUIRE(packed && scales && biases && w, QLQ_ERR_INVALID_ARG, "null pointer");
+  if (int st = check_affine_shape(N, K, bits, group_size)) return st;
+  QLQ_REQUIRE(dtype_ok(sb_dtype), QLQ_ERR_UNSUPPORTED, "sb_dtype %d", sb_dtype);
+  QLQ_REQUIRE(aligned(packed, 4) && aligned(w, 4) && aligned(scales, dtype_size(sb_dtype)) &&
+                  aligned(biases, dtype_size(sb_dtype)),
+              QLQ_ERR_ALIGNMENT, "misaligned pointer");
+  if (int st = current_device_status()) return st;
+  return hip_status(qlq::launch_affine_dequant(packed, scales, biases, sb_dtype, N, K, bits, group_size, w,
+                                               (hipStream_t)stream),
+                    "dequantize");
+}
+
+QLQ_API size_t qlq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int bits, int group_size,
+                                         int x_dtype) {
+  (void)bits;
+  if (M <= 0 || K <= 0 || N <= 0 || group_size <= 0 || K % group_size) return 0;
+  if (!takes_gemm(M, K, x_dtype)) return 0;
+  return qlq::affine_gemm_workspace(M, K, N);
+}
+
+QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
+                               const void* scales, const void* biases, int sb_dtype, int64_t N, int bits,
+                               int group_size, const void* bias, void* y, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  QLQ_REQUIRE(x && packed && scales && biases && y, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(M >= 0 && M < kMaxDim, QLQ_ERR_INVALID_ARG, "invalid M=%lld", (long long)M);
+  if (int st = check_affine_shape(N, K, bits, group_size)) return st;
+  QLQ_REQUIRE(dtype_ok(x_dtype), QLQ_ERR_UNSUPPORTED, "x_dtype %d", x_dtype);
+  QLQ_REQUIRE(sb_dtype == x_dtype, QLQ_ERR_DTYPE, "scales/biases dtype %d != x dtype %d", sb_dtype, x_dtype);
+  const size_t es = dtype_size(x_dtype);
+  QLQ_REQUIRE(aligned(x, 16) && aligned(packed, 16), QLQ_ERR_ALIGNMENT, "x / packed not 16-byte aligned");
+  QLQ_REQUIRE(aligned(scales, es) && aligned(biases, es) && aligned(y, es) && (!bias || aligned(bias, es)),
+              QLQ_ERR_ALIGNMENT, "misaligned scales / biases / bias / y");
+  const bool gemm = takes_gemm(M, K, x_dtype);
+  if (gemm) {
+    const size_t need = qlq::affine_gemm_workspace(M, K, N);
+    QLQ_REQUIRE(workspace && workspace_bytes >= need, QLQ_ERR_WORKSPACE,
+                "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+    QLQ_REQUIRE(aligned(workspace, 256), QLQ_ERR_ALIGNMENT, "workspace not 256-byte aligned");
+  } else {
+    QLQ_REQUIRE((M + 7) / 8 <= 65535, QLQ_ERR_UNSUPPORTED, "M too large for the skinny kernel");
+  }
+  if (M == 0) return ok();
+  if (int st = current_device_status()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (gemm)
+    return hip_status(qlq::launch_affine_gemm(x, x_dtype, M, K, packed, scales, biases, N, bits, group_size,
+                                              bias, y, workspace, s),
+                      "affine gemm");
+  return hip_status(qlq::launch_affine_gemv(x, x_dtype, M, K, packed, scales, biases, N, bits, group_size,
+                                            bias, y, s),
+                    "affine gemv");
+}
+
+// ---------------------------------------------------------------- ternary
+QLQ_API int bitlinear_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* packed, void* stream) {
+  QLQ_REQUIRE(t && packed, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(N >= 4 && K >= 1 && N < kMaxDim && K < kMaxDim, QLQ_ERR_INVALID_ARG, "invalid shape");
+  QLQ_REQUIRE(N % 4 == 0, QLQ_ERR_INVALID_ARG, "N=%lld is not a multiple of 4", (long long)N);
+  if (int st = current_device_status()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  DevFlag flag;
+  if (int st = hip_status(hipMalloc((void**)&flag.p, sizeof(int)), "hipMalloc(flag)")) return st;
+  if (int st = hip_status(hipMemsetAsync(flag.p, 0, sizeof(int), s), "hipMemsetAsync")) return st;
+  if (int st = hip_status(qlq::launch_ternary_pack(t, N, K, packed, flag.p, s), "ternary_pack launch"))
+    return st;
+  int host_flag = 0;
+  if (int st = hip_status(hipMemcpyAsync(&host_flag, flag.p, sizeof(int), hipMemcpyDeviceToHost, s),
+                          "hipMemcpyAsync(flag)"))
+    return st;
+  if (int st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize")) return st;
+  QLQ_REQUIRE(host_flag == 0, QLQ_ERR_DATA, "ternary value outside {-1, 0, 1}");
+  return ok();
+}
+
+QLQ_API int bitlinear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
+                              int64_t N, const void* weight_scale, int invert_weight_scale, const void* bias,
+                              void* y, void* stream) {
+  QLQ_REQUIRE(x && packed && weight_scale && y, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(M >= 0 && M < kMaxDim && N >= 4 && N < kMaxDim && K >= 1 && K < kMaxDim, QLQ_ERR_INVALID_ARG,
+              "invalid shape");
+  QLQ_REQUIRE(N % 4 == 0, QLQ_ERR_INVALID_ARG, "N=%lld is not a multiple of 4", (long long)N);
+  QLQ_REQUIRE(K % 32 == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 32", (long long)K);
+  QLQ_REQUIRE(dtype_ok(x_dtype), QLQ_ERR_UNSUPPORTED, "x_dtype %d", x_dtype);
+  const size_t es = dtype_size(x_dtype);
+  QLQ_REQUIRE(aligned(x, 16) && aligned(packed, 16), QLQ_ERR_ALIGNMENT, "x / packed not 16-byte aligned");
+  QLQ_REQUIRE(aligned(weight_scale, es) && aligned(y, es) && (!bias || aligned(bias, es)),
+              QLQ_ERR_ALIGNMENT, "misaligned weight_scale / bias / y");
+  QLQ_REQUIRE((M + 15) / 16 <= 65535, QLQ_ERR_UNSUPPORTED, "M too large for one launch");
+  if (M == 0) return ok();
+  if (int st = current_device_status()) return st;
+  return hip_status(qlq::launch_ternary_forward(x, x_dtype, M, K, packed, N, weight_scale,
+                                                invert_weight_scale, bias, y, (hipStream_t)stream),
+                    "ternary forward");
+}
+
+// ------------------------------------------------------------------- W8A8
+QLQ_API int qlq_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_t K, int8_t* q, float* scale,
+                                   void* stream) {
+  QLQ_REQUIRE(v && q && scale, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(R >= 0 && R < kMaxDim && K >= 16 && K < kMaxDim, QLQ_ERR_INVALID_ARG, "invalid shape");
+  QLQ_REQUIRE(K % 16 == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
+  QLQ_REQUIRE(dtype_ok(v_dtype), QLQ_ERR_UNSUPPORTED, "v_dtype %d", v_dtype);
+  QLQ_REQUIRE(aligned(v, 16) && aligned(q, 16) && aligned(scale, 4), QLQ_ERR_ALIGNMENT, "misaligned pointer");
+  if (R == 0) return ok();
+  if (int st = current_device_status()) return st;
+  return hip_status(qlq::launch_quantize_rows_int8(v, v_dtype, R, K, q, scale, (hipStream_t)stream),
+                    "quantize rows");
+}
+
+QLQ_API int qlq_int8_matmul_int32(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K, int32_t* c,
+                                  void* stream) {
+  QLQ_REQUIRE(a && b && c, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(M >= 0 && M < kMaxDim && N >= 1 && N < kMaxDim && K >= 16, QLQ_ERR_INVALID_ARG, "invalid shape");
+  QLQ_REQUIRE(K % 16 == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
+  QLQ_REQUIRE(K <= 131071, QLQ_ERR_UNSUPPORTED, "K=%lld could overflow int32", (long long)K);
+  QLQ_REQUIRE(aligned(a, 16) && aligned(b, 16) && aligned(c, 4), QLQ_ERR_ALIGNMENT, "misaligned pointer");
+  QLQ_REQUIRE((M + 127) / 128 <= 65535, QLQ_ERR_UNSUPPORTED, "M too large for one launch");
+  if (M == 0) return ok();
+  if (int st = current_device_status()) return st;
+  return hip_status(qlq::launch_int8_gemm(a, b, M, N, K, nullptr, nullptr, nullptr, -1, c, (hipStream_t)stream),
+                    "int8 gemm");
+}
+
+QLQ_API size_t w8a8_workspace_size(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
+  const size_t q = ((size_t)M * (size_t)K + 255) & ~(size_t)255;
+  return q + (size_t)M * sizeof(float);
+}
+
+QLQ_API int w8a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* w,
+                                const float* scale_w, int64_t N, const void* bias, void* y, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  QLQ_REQUIRE(x && w && scale_w && y, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(M >= 0 && M < kMaxDim && N >= 1 && N < kMaxDim && K >= 16, QLQ_ERR_INVALID_ARG, "invalid shape");
+  QLQ_REQUIRE(K % 16 == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
+  QLQ_REQUIRE(K <= 131071, QLQ_ERR_UNSUPPORTED, "K=%lld could overflow int32", (long long)K);
+  QLQ_REQUIRE(x_dtype == QLQ_F16 || x_dtype == QLQ_BF16, QLQ_ERR_UNSUPPORTED, "x_dtype must be F16 or BF16");
+  QLQ_REQUIRE(aligned(x, 16) && aligned(w, 16) && aligned(scale_w, 4) && aligned(y, 2) &&
+                  (!bias || aligned(bias, 2)),
+              QLQ_ERR_ALIGNMENT, "misaligned pointer");
+  QLQ_REQUIRE((M + 127) / 128 <= 65535, QLQ_ERR_UNSUPPORTED, "M too large for one launch");
+  if (M == 0) return ok();
+  const size_t need = w8a8_workspace_size(M, K);
+  QLQ_REQUIRE(workspace && workspace_bytes >= need, QLQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+              need, workspace ? workspace_bytes : (size_t)0);
+  QLQ_REQUIRE(aligned(workspace, 16), QLQ_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+  if (int st = current_device_status()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  int8_t* xq = (int8_t*)workspace;
+  float* sx = (float*)((char*)workspace + (((size_t)M * (size_t)K + 255) & ~(size_t)255));
+  if (int st = hip_status(qlq::launch_quantize_rows_int8(x, x_dtype, M, K, xq, sx, s), "activation quant"))
+    return st;
+  return hip_status(qlq::launch_int8_gemm(xq, w, M, N, K, sx, scale_w, bias, x_dtype, y, s), "int8 gemm");
+}
+
+}  // extern "C"

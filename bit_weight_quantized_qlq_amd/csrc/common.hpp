@@ -1,0 +1,98 @@
+// Shared device helpers for the qlq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlq {
+
+// Storage dtype codes (match enum qlq_dtype in qlq.h).
+enum DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+typedef _Float16 f16_t;
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_v;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_v;
+typedef __attribute__((ext_vector_type(4))) float f32x4_v;
+typedef __attribute__((ext_vector_type(16))) float f32x16_v;
+typedef __attribute__((ext_vector_type(4))) int i32x4_v;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_v;  // 16 bytes in registers
+
+constexpr int kWave = 64;
+
+// ---- scalar conversions ------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN -> quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Typed element access for the three storage dtypes.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+  static __device__ __forceinline__ float round(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(bf16_t* p, int64_t i, float v) { p[i] = (bf16_t)f32_to_bf16_rne(v); }
+  static __device__ __forceinline__ float round(float v) { return bf16_to_f32(f32_to_bf16_rne(v)); }
+};
+template <> struct Elem<f16_t> {
+  static __device__ __forceinline__ float load(const f16_t* p, int64_t i) { return (float)p[i]; }
+  static __device__ __forceinline__ void store(f16_t* p, int64_t i, float v) { p[i] = (f16_t)v; }
+  static __device__ __forceinline__ float round(float v) { return (float)(f16_t)v; }
+};
+
+// 16-bit storage bits -> fp32 value for a 16-bit storage type.
+template <typename T> __device__ __forceinline__ float bits16_to_f32(uint16_t h);
+template <> __device__ __forceinline__ float bits16_to_f32<bf16_t>(uint16_t h) { return bf16_to_f32(h); }
+template <> __device__ __forceinline__ float bits16_to_f32<f16_t>(uint16_t h) {
+  return (float)__builtin_bit_cast(f16_t, h);
+}
+
+__device__ __forceinline__ bool is_finite_f32(float v) {
+  return (__float_as_uint(v) & 0x7F800000u) != 0x7F800000u;
+}
+
+// ---- wave reductions (wave64) ---------------------------------------------
+// DPP sum: two quad permutes and two row rotates leave every lane of each
+// 16-lane row holding the row's sum; four readlanes add the rows.  The result
+// is uniform across the wave.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x124>(v);  // row_ror:4
+  v += dpp_f32<0x128>(v);  // row_ror:8
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace qlq

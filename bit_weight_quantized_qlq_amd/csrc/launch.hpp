@@ -1,0 +1,48 @@
+// Host-side launchers of the qlq kernels.  Each returns the hipError_t of its
+// launch; the C ABI layer (api.cpp) validates arguments before calling them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qlq {
+
+// pack.hip
+hipError_t launch_affine_pack(const float* w, int64_t N, int64_t K, int bits, int G,
+                              uint32_t* packed, void* scales, void* biases, int sb_dtype,
+                              int* err_flag, hipStream_t s);
+hipError_t launch_affine_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits,
+                                uint8_t* codes, hipStream_t s);
+hipError_t launch_affine_dequant(const uint32_t* packed, const void* scales, const void* biases,
+                                 int sb_dtype, int64_t N, int64_t K, int bits, int G, float* w,
+                                 hipStream_t s);
+hipError_t launch_ternary_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* packed,
+                               int* err_flag, hipStream_t s);
+hipError_t launch_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_t K,
+                                     int8_t* q, float* scale, hipStream_t s);
+
+// gemv.hip: skinny affine forward (small M)
+hipError_t launch_affine_gemv(const void* x, int x_dtype, int64_t M, int64_t K,
+                              const uint32_t* packed, const void* scales, const void* biases,
+                              int64_t N, int bits, int G, const void* bias, void* y,
+                              hipStream_t s);
+
+// gemm.hip: affine prefill GEMM (bf16 / f16 x)
+size_t affine_gemm_workspace(int64_t M, int64_t K, int64_t N);
+hipError_t launch_affine_gemm(const void* x, int x_dtype, int64_t M, int64_t K,
+                              const uint32_t* packed, const void* scales, const void* biases,
+                              int64_t N, int bits, int G, const void* bias, void* y,
+                              void* workspace, hipStream_t s);
+
+// ternary.hip
+hipError_t launch_ternary_forward(const void* x, int x_dtype, int64_t M, int64_t K,
+                                  const uint8_t* packed, int64_t N, const void* weight_scale,
+                                  int invert, const void* bias, void* y, hipStream_t s);
+
+// int8.hip
+hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K,
+                            const float* sa, const float* sb, const void* bias, int out_dtype,
+                            void* out, hipStream_t s);
+
+}  // namespace qlq

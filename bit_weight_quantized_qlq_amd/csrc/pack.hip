@@ -1,0 +1,301 @@
+// Bit-exact quantize / pack / unpack / dequantize kernels.
+//
+// Affine format: "Struct QuantizedLinear" (nuvec-nn docs), Fields and
+// from_linear; formula from the MLX affine docstring of pergroup_linear in
+// "cider/ops.py".  Ternary format: make_bitlinear_kernel in
+// "mlx-lm/mlx_lm/models/bitlinear_layers.py".  Row int8 quantizer:
+// quantize_weight_int8 (absmax branch) in "cider/ops.py".
+//
+// Every floating-point step that decides an integer is a single IEEE fp32
+// operation with round-to-nearest-even (__fsub_rn, __fdiv_rn, rintf), so the
+// codes equal those of an fp32 reference bit for bit.  These kernels are off
+// the timed path; they favour plain indexing over peak bandwidth.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace qlq {
+
+// ---------------------------------------------------------------- affine pack
+// One thread per (row n, group g).  The thread reads its G weights, forms the
+// fp32 min/max, the stored scale and bias, and writes G*bits/32 packed words.
+template <int BITS, typename SB>
+__global__ void __launch_bounds__(256)
+affine_pack_kernel(const float* __restrict__ w, int64_t N, int64_t K, int G,
+                   uint32_t* __restrict__ packed, SB* __restrict__ scales,
+                   SB* __restrict__ biases, int* __restrict__ err) {
+  const int64_t ngroups = K / G;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= N * ngroups) return;
+  const int64_t n = t / ngroups, g = t % ngroups;
+  const float* wg = w + n * K + g * G;
+  constexpr uint32_t qmax = (1u << BITS) - 1u;
+
+  float mn = wg[0], mx = wg[0];
+  bool finite = true;
+  for (int i = 0; i < G; i += 4) {
+    float4 v = *reinterpret_cast<const float4*>(wg + i);
+    finite &= is_finite_f32(v.x) & is_finite_f32(v.y) & is_finite_f32(v.z) & is_finite_f32(v.w);
+    mn = fminf(mn, fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
+    mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+  }
+  // scale = (max - min) / (2^b - 1), bias = min; both rounded to the storage dtype
+  const float s32 = __fdiv_rn(__fsub_rn(mx, mn), (float)qmax);
+  float s = Elem<SB>::round(s32);
+  const float b = Elem<SB>::round(mn);
+  finite &= is_finite_f32(s) & is_finite_f32(b);
+  if (!finite) atomicOr(err, 1);
+  if (s == 0.0f) s = 1.0f;
+  Elem<SB>::store(scales, t, s);
+  Elem<SB>::store(biases, t, b);
+
+  constexpr int per = 32 / BITS;
+  uint32_t* out = packed + (n * K + g * G) / per;
+  for (int i = 0; i < G; i += per) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      float q = rintf(__fdiv_rn(__fsub_rn(wg[i + j], b), s));
+      q = fminf(fmaxf(q, 0.0f), (float)qmax);
+      word |= (uint32_t)q << (BITS * j);
+    }
+    out[i / per] = word;
+  }
+}
+
+template <int BITS>
+static hipError_t pack_dispatch_sb(const float* w, int64_t N, int64_t K, int G, uint32_t* packed,
+                                   void* scales, void* biases, int sb, int* err, hipStream_t s) {
+  const int64_t total = N * (K / G);
+  dim3 grid((unsigned)cdiv(total, 256)), block(256);
+  switch (sb) {
+    case F32:
+      hipLaunchKernelGGL((affine_pack_kernel<BITS, float>), grid, block, 0, s, w, N, K, G, packed,
+                         (float*)scales, (float*)biases, err);
+      break;
+    case BF16:
+      hipLaunchKernelGGL((affine_pack_kernel<BITS, bf16_t>), grid, block, 0, s, w, N, K, G, packed,
+                         (bf16_t*)scales, (bf16_t*)biases, err);
+      break;
+    default:
+      hipLaunchKernelGGL((affine_pack_kernel<BITS, f16_t>), grid, block, 0, s, w, N, K, G, packed,
+                         (f16_t*)scales, (f16_t*)biases, err);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_affine_pack(const float* w, int64_t N, int64_t K, int bits, int G,
+                              uint32_t* packed, void* scales, void* biases, int sb_dtype,
+                              int* err_flag, hipStream_t s) {
+  switch (bits) {
+    case 2: return pack_dispatch_sb<2>(w, N, K, G, packed, scales, biases, sb_dtype, err_flag, s);
+    case 4: return pack_dispatch_sb<4>(w, N, K, G, packed, scales, biases, sb_dtype, err_flag, s);
+    default: return pack_dispatch_sb<8>(w, N, K, G, packed, scales, biases, sb_dtype, err_flag, s);
+  }
+}
+
+// -------------------------------------------------------------- affine unpack
+template <int BITS>
+__global__ void __launch_bounds__(256)
+affine_unpack_kernel(const uint32_t* __restrict__ packed, int64_t nwords, uint8_t* __restrict__ codes) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nwords) return;
+  constexpr int per = 32 / BITS;
+  const uint32_t word = packed[t];
+#pragma unroll
+  for (int j = 0; j < per; ++j) codes[t * per + j] = (uint8_t)((word >> (BITS * j)) & ((1u << BITS) - 1u));
+}
+
+hipError_t launch_affine_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits,
+                                uint8_t* codes, hipStream_t s) {
+  const int64_t nwords = N * K * bits / 32;
+  dim3 grid((unsigned)cdiv(nwords, 256)), block(256);
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(affine_unpack_kernel<2>, grid, block, 0, s, packed, nwords, codes); break;
+    case 4: hipLaunchKernelGGL(affine_unpack_kernel<4>, grid, block, 0, s, packed, nwords, codes); break;
+    default: hipLaunchKernelGGL(affine_unpack_kernel<8>, grid, block, 0, s, packed, nwords, codes); break;
+  }
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------- affine dequantize
+// w = fma(scale, q, bias): one rounding of the exact value, in fp32.
+template <int BITS, typename SB>
+__global__ void __launch_bounds__(256)
+affine_dequant_kernel(const uint32_t* __restrict__ packed, const SB* __restrict__ scales,
+                      const SB* __restrict__ biases, int64_t N, int64_t K, int G,
+                      float* __restrict__ w) {
+  constexpr int per = 32 / BITS;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t words_per_row = K / per;
+  if (t >= N * words_per_row) return;
+  const int64_t n = t / words_per_row, k0 = (t % words_per_row) * per;
+  const int64_t gi = n * (K / G) + k0 / G;  // a word never straddles a group (G % per == 0)
+  const float s = Elem<SB>::load(scales, gi), b = Elem<SB>::load(biases, gi);
+  const uint32_t word = packed[t];
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    const float q = (float)((word >> (BITS * j)) & ((1u << BITS) - 1u));
+    w[n * K + k0 + j] = __fmaf_rn(s, q, b);
+  }
+}
+
+template <int BITS>
+static hipError_t dequant_dispatch_sb(const uint32_t* packed, const void* scales, const void* biases,
+                                      int sb, int64_t N, int64_t K, int G, float* w, hipStream_t s) {
+  const int64_t total = N * K * BITS / 32;
+  dim3 grid((unsigned)cdiv(total, 256)), block(256);
+  switch (sb) {
+    case F32:
+      hipLaunchKernelGGL((affine_dequant_kernel<BITS, float>), grid, block, 0, s, packed,
+                         (const float*)scales, (const float*)biases, N, K, G, w);
+      break;
+    case BF16:
+      hipLaunchKernelGGL((affine_dequant_kernel<BITS, bf16_t>), grid, block, 0, s, packed,
+                         (const bf16_t*)scales, (const bf16_t*)biases, N, K, G, w);
+      break;
+    default:
+      hipLaunchKernelGGL((affine_dequant_kernel<BITS, f16_t>), grid, block, 0, s, packed,
+                         (const f16_t*)scales, (const f16_t*)biases, N, K, G, w);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_affine_dequant(const uint32_t* packed, const void* scales, const void* biases,
+                                 int sb_dtype, int64_t N, int64_t K, int bits, int G, float* w,
+                                 hipStream_t s) {
+  switch (bits) {
+    case 2: return dequant_dispatch_sb<2>(packed, scales, biases, sb_dtype, N, K, G, w, s);
+    case 4: return dequant_dispatch_sb<4>(packed, scales, biases, sb_dtype, N, K, G, w, s);
+    default: return dequant_dispatch_sb<8>(packed, scales, biases, sb_dtype, N, K, G, w, s);
+  }
+}
+
+// ---------------------------------------------------------------- ternary pack
+// byte[r, k] = sum_j (t[r + j*R, k] + 1) << 2j  with R = N/4.
+__global__ void __launch_bounds__(256)
+ternary_pack_kernel(const int8_t* __restrict__ t, int64_t R, int64_t K, uint8_t* __restrict__ packed,
+                    int* __restrict__ err) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= R * K) return;
+  const int64_t r = i / K, k = i % K;
+  uint32_t byte = 0;
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int v = t[(r + j * R) * K + k];
+    ok &= (v >= -1) & (v <= 1);
+    byte |= (uint32_t)((v + 1) & 3) << (2 * j);
+  }
+  if (!ok) atomicOr(err, 1);
+  packed[i] = (uint8_t)byte;
+}
+
+hipError_t launch_ternary_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* packed, int* err_flag,
+                               hipStream_t s) {
+  const int64_t R = N / 4;
+  dim3 grid((unsigned)cdiv(R * K, 256)), block(256);
+  hipLaunchKernelGGL(ternary_pack_kernel, grid, block, 0, s, t, R, K, packed, err_flag);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ row int8 quantization
+// One 256-thread block per row.  Pass 1: exact fp32 absmax (block reduction).
+// Pass 2: q = clamp(rint(v / s), -128, 127) with s = a / 127 (1 if 0).
+// Each thread handles 16 consecutive elements per step (K % 16 == 0).
+template <typename T>
+__device__ __forceinline__ void load16(const T* p, float (&v)[16]);
+template <>
+__device__ __forceinline__ void load16<float>(const float* p, float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float4 f = reinterpret_cast<const float4*>(p)[i];
+    v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+  }
+}
+template <>
+__device__ __forceinline__ void load16<bf16_t>(const bf16_t* p, float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    uint4 u = reinterpret_cast<const uint4*>(p)[i];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+}
+template <>
+__device__ __forceinline__ void load16<f16_t>(const f16_t* p, float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    f16x8_v h = reinterpret_cast<const f16x8_v*>(p)[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[8 * i + j] = (float)h[j];
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+quantize_rows_int8_kernel(const T* __restrict__ v, int64_t K, int8_t* __restrict__ q,
+                          float* __restrict__ scale) {
+  __shared__ float red[256 / kWave];
+  const int64_t row = blockIdx.x;
+  const T* vr = v + row * K;
+  int8_t* qr = q + row * K;
+  const int tid = threadIdx.x;
+
+  float a = 0.0f;
+  for (int64_t k = (int64_t)tid * 16; k < K; k += 256 * 16) {
+    float e[16];
+    load16<T>(vr + k, e);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(e[i]));
+  }
+  a = wave_max(a);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float s = __fdiv_rn(a, 127.0f);
+  if (s == 0.0f) s = 1.0f;
+  if (tid == 0) scale[row] = s;
+
+  for (int64_t k = (int64_t)tid * 16; k < K; k += 256 * 16) {
+    float e[16];
+    load16<T>(vr + k, e);
+    uint32_t packed4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float r = rintf(__fdiv_rn(e[4 * i + j], s));
+        r = fminf(fmaxf(r, -128.0f), 127.0f);
+        word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
+      }
+      packed4[i] = word;
+    }
+    *reinterpret_cast<uint4*>(qr + k) = make_uint4(packed4[0], packed4[1], packed4[2], packed4[3]);
+  }
+}
+
+hipError_t launch_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_t K, int8_t* q,
+                                     float* scale, hipStream_t s) {
+  dim3 grid((unsigned)R), block(256);
+  switch (v_dtype) {
+    case F32:
+      hipLaunchKernelGGL(quantize_rows_int8_kernel<float>, grid, block, 0, s, (const float*)v, K, q, scale);
+      break;
+    case BF16:
+      hipLaunchKernelGGL(quantize_rows_int8_kernel<bf16_t>, grid, block, 0, s, (const bf16_t*)v, K, q, scale);
+      break;
+    default:
+      hipLaunchKernelGGL(quantize_rows_int8_kernel<f16_t>, grid, block, 0, s, (const f16_t*)v, K, q, scale);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qlq

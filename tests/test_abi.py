@@ -1,0 +1,165 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/qlq.h declares, and rejects invalid arguments before any HIP call.
+
+Pointers here are fake non-null addresses.  Each invalid call has exactly one
+invalid aspect that host validation rejects, so no call reaches the device.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import bit_weight_quantized_qlq_amd as qlq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlq.h")
+
+A = 0x100000    # 16-byte aligned fake device address
+B = 0x200000
+ODD = 0x100002  # 2-byte aligned only
+
+pytestmark = pytest.mark.skipif(not os.path.exists(qlq.lib_path()), reason="libqlq.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"QLQ_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_matches_binding_and_exports():
+    names = _declared()
+    assert len(names) >= 15
+    assert set(names) == set(qlq.SIGNATURES), set(names) ^ set(qlq.SIGNATURES)
+    handle = ctypes.CDLL(qlq.lib_path())
+    for n in names:
+        assert hasattr(handle, n), n
+
+
+def test_version_and_threshold():
+    L = qlq.lib()
+    assert b"gfx950" in L.qlq_version()
+    old = L.qlq_get_skinny_max_m()
+    assert L.qlq_set_skinny_max_m(-1) == qlq.QLQ_ERR_INVALID_ARG
+    assert L.qlq_set_skinny_max_m(3) == 0 and L.qlq_get_skinny_max_m() == 3
+    assert L.qlq_set_skinny_max_m(old) == 0
+
+
+def _lin(**kw):
+    a = dict(x=A, x_dtype=qlq.QLQ_BF16, M=4, K=256, packed=A, scales=A, biases=A,
+             sb_dtype=qlq.QLQ_BF16, N=64, bits=4, G=64, bias=None, y=A, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return qlq.lib().qlq_linear_forward(a["x"], a["x_dtype"], a["M"], a["K"], a["packed"], a["scales"],
+                                        a["biases"], a["sb_dtype"], a["N"], a["bits"], a["G"], a["bias"],
+                                        a["y"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), qlq.QLQ_ERR_INVALID_ARG),
+    (dict(y=None), qlq.QLQ_ERR_INVALID_ARG),
+    (dict(M=-1), qlq.QLQ_ERR_INVALID_ARG),
+    (dict(N=0), qlq.QLQ_ERR_INVALID_ARG),
+    (dict(K=250), qlq.QLQ_ERR_INVALID_ARG),          # K % G != 0
+    (dict(bits=3), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(bits=5), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(G=48), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(G=256, K=512), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(x_dtype=7, sb_dtype=7), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(sb_dtype=qlq.QLQ_F32), qlq.QLQ_ERR_DTYPE),
+    (dict(x=ODD), qlq.QLQ_ERR_ALIGNMENT),
+    (dict(packed=ODD), qlq.QLQ_ERR_ALIGNMENT),
+    (dict(y=A + 1), qlq.QLQ_ERR_ALIGNMENT),
+    (dict(M=4096), qlq.QLQ_ERR_WORKSPACE),            # GEMM path without workspace
+    (dict(M=4096, ws=A, ws_bytes=16), qlq.QLQ_ERR_WORKSPACE),
+])
+def test_linear_forward_validation(kw, code):
+    assert _lin(**kw) == code
+    assert qlq.last_error() != ""
+
+
+def test_workspace_sizes():
+    L = qlq.lib()
+    # skinny path needs none; GEMM path needs the group-sum split
+    assert L.qlq_linear_workspace_size(1, 4096, 4096, 4, 64, qlq.QLQ_BF16) == 0
+    assert L.qlq_linear_workspace_size(2048, 4096, 4096, 4, 64, qlq.QLQ_F32) == 0
+    ws = L.qlq_linear_workspace_size(2048, 4096, 11008, 4, 128, qlq.QLQ_BF16)
+    assert ws >= 2048 * 6 * 32 * 2 + 2048 * 4
+    assert L.w8a8_workspace_size(1024, 4096) >= 1024 * 4096 + 1024 * 4
+    assert L.w8a8_workspace_size(0, 4096) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 8, 64, 4, 64, A, A, A, qlq.QLQ_BF16, None), qlq.QLQ_ERR_INVALID_ARG),
+    ((A, 8, 64, 3, 64, A, A, A, qlq.QLQ_BF16, None), qlq.QLQ_ERR_UNSUPPORTED),
+    ((A, 8, 64, 4, 16, A, A, A, qlq.QLQ_BF16, None), qlq.QLQ_ERR_UNSUPPORTED),
+    ((A, 8, 96, 4, 64, A, A, A, qlq.QLQ_BF16, None), qlq.QLQ_ERR_INVALID_ARG),
+    ((A, 8, 64, 4, 64, A, A, A, 9, None), qlq.QLQ_ERR_UNSUPPORTED),
+    ((ODD, 8, 64, 4, 64, A, A, A, qlq.QLQ_BF16, None), qlq.QLQ_ERR_ALIGNMENT),
+])
+def test_pack_validation(args, code):
+    assert qlq.lib().qlq_pack(*args) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=6), qlq.QLQ_ERR_INVALID_ARG),           # N % 4
+    (dict(K=48), qlq.QLQ_ERR_INVALID_ARG),          # K % 32
+    (dict(ws=None), qlq.QLQ_ERR_INVALID_ARG),
+    (dict(x_dtype=5), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(x=ODD), qlq.QLQ_ERR_ALIGNMENT),
+    (dict(y=A + 1), qlq.QLQ_ERR_ALIGNMENT),
+])
+def test_bitlinear_validation(kw, code):
+    a = dict(x=A, x_dtype=qlq.QLQ_BF16, M=8, K=64, packed=A, N=16, ws=B, inv=0, bias=None, y=A)
+    a.update(kw)
+    r = qlq.lib().bitlinear_forward(a["x"], a["x_dtype"], a["M"], a["K"], a["packed"], a["N"], a["ws"],
+                                    a["inv"], a["bias"], a["y"], None)
+    assert r == code
+
+
+def test_bitlinear_pack_validation():
+    assert qlq.lib().bitlinear_pack(A, 6, 8, A, None) == qlq.QLQ_ERR_INVALID_ARG
+    assert qlq.lib().bitlinear_pack(None, 8, 8, A, None) == qlq.QLQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=40), qlq.QLQ_ERR_INVALID_ARG),
+    (dict(K=131072), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(x_dtype=qlq.QLQ_F32), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(ws=None), qlq.QLQ_ERR_WORKSPACE),
+    (dict(ws_bytes=100), qlq.QLQ_ERR_WORKSPACE),
+    (dict(x=ODD), qlq.QLQ_ERR_ALIGNMENT),
+    (dict(w=A + 8), qlq.QLQ_ERR_ALIGNMENT),
+])
+def test_w8a8_validation(kw, code):
+    a = dict(x=A, x_dtype=qlq.QLQ_F16, M=16, K=64, w=B, sw=A, N=32, bias=None, y=A, ws=B, ws_bytes=1 << 20)
+    a.update(kw)
+    r = qlq.lib().w8a8_linear_forward(a["x"], a["x_dtype"], a["M"], a["K"], a["w"], a["sw"], a["N"],
+                                      a["bias"], a["y"], a["ws"], a["ws_bytes"], None)
+    assert r == code
+
+
+def test_int8_helpers_validation():
+    L = qlq.lib()
+    assert L.qlq_int8_matmul_int32(A, B, 4, 4, 40, A, None) == qlq.QLQ_ERR_INVALID_ARG
+    assert L.qlq_int8_matmul_int32(A, B, 4, 4, 131088, A, None) == qlq.QLQ_ERR_UNSUPPORTED
+    assert L.qlq_int8_matmul_int32(ODD, B, 4, 4, 64, A, None) == qlq.QLQ_ERR_ALIGNMENT
+    assert L.qlq_quantize_rows_int8(A, qlq.QLQ_F16, 4, 40, A, A, None) == qlq.QLQ_ERR_INVALID_ARG
+    assert L.qlq_quantize_rows_int8(A, 11, 4, 64, A, A, None) == qlq.QLQ_ERR_UNSUPPORTED
+    assert L.qlq_unpack(A, 4, 64, 3, A, None) == qlq.QLQ_ERR_UNSUPPORTED
+    assert L.qlq_dequantize(A, A, A, qlq.QLQ_BF16, 4, 64, 4, 48, A, None) == qlq.QLQ_ERR_UNSUPPORTED
+
+
+def test_empty_batch_is_a_no_op():
+    # M == 0 returns before any device work, on any machine
+    assert _lin(M=0) == 0
+    assert qlq.lib().w8a8_linear_forward(A, qlq.QLQ_F16, 0, 64, B, A, 32, None, A, None, 0, None) == 0
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
+def test_valid_call_without_device_reports_device_error():
+    # fully valid arguments: validation passes, then the device check fails
+    assert _lin() == qlq.QLQ_ERR_DEVICE
+    assert qlq.lib().qlq_device_check(0) == qlq.QLQ_ERR_DEVICE
+    assert "device" in qlq.last_error()

@@ -1,0 +1,95 @@
+"""GPU parity for W8A8: row int8 quantization and the int32 accumulators are
+bit-exact against the oracle; the scaled output is within the tolerance rule."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import bit_weight_quantized_qlq_amd as qlq
+from parity import ODT, assert_close, dev, f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("vdt", [torch.float16, torch.bfloat16, torch.float32])
+def test_quantize_rows_bitexact(vdt):
+    inp = workloads.w8a8_inputs(97, 4096 + 64, 8, x_dtype=ODT[vdt], seed=21)
+    v = inp["x"]
+    v[5] = 0  # a zero row takes scale 1
+    q, s = qlq.qlq_quantize_rows_int8(v.to(dev()))
+    q_ref, s_ref = oracle.quantize_rows_int8(f32(v))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_quantize_rows_workload_bitexact():
+    inp = workloads.workload_inputs("w8a8_perchannel")
+    q, s = qlq.qlq_quantize_rows_int8(inp["x"].to(dev()))
+    q_ref, s_ref = oracle.quantize_rows_int8(f32(inp["x"]))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    # weights go through the same quantizer
+    qw, sw = qlq.qlq_quantize_rows_int8(inp["w"].to(dev()))
+    qw_ref, sw_ref = oracle.quantize_rows_int8(inp["w"].numpy())
+    assert np.array_equal(qw.cpu().numpy(), qw_ref)
+    assert np.array_equal(sw.cpu().numpy(), sw_ref)
+
+
+@pytest.mark.parametrize("shape", [(77, 45, 208), (1, 1, 16), (128, 128, 128), (130, 257, 4096 + 16)])
+def test_int8_matmul_bitexact(shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M + N + K)
+    a = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
+    b = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    c = qlq.qlq_int8_matmul_int32(torch.from_numpy(a).to(dev()), torch.from_numpy(b).to(dev()))
+    assert np.array_equal(c.cpu().numpy().astype(np.int64), oracle.int8_matmul_int32(a, b))
+
+
+def test_int8_matmul_extremes():
+    K = 4096
+    a = torch.full((3, K), -128, dtype=torch.int8, device=dev())
+    b = torch.full((5, K), -128, dtype=torch.int8, device=dev())
+    b[1] = 127
+    c = qlq.qlq_int8_matmul_int32(a, b)
+    assert (c[:, 0] == 2 ** 26).all() and (c[:, 1] == -128 * 127 * K).all()
+
+
+def test_int8_matmul_workload_sampled_rows():
+    inp = workloads.workload_inputs("w8a8_perchannel")
+    xq, _ = qlq.qlq_quantize_rows_int8(inp["x"].to(dev()))
+    wq, _ = qlq.qlq_quantize_rows_int8(inp["w"].to(dev()))
+    c = qlq.qlq_int8_matmul_int32(xq, wq)
+    rows = [0, 1, 63, 64, 511, 512, 1022, 1023] + list(np.random.default_rng(2).choice(1024, 8, replace=False))
+    ref = oracle.int8_matmul_int32(xq.cpu().numpy()[rows], wq.cpu().numpy())
+    assert np.array_equal(c.cpu().numpy()[rows].astype(np.int64), ref)
+
+
+def _w8a8_case(inp, rows=None):
+    x, w, bias = inp["x"], inp["w"], inp["bias"]
+    wq, sw = qlq.qlq_quantize_rows_int8(w.to(dev()))
+    y = qlq.w8a8_linear_forward(x.to(dev()), wq, sw, bias=None if bias is None else bias.to(dev()))
+    torch.cuda.synchronize()
+    wq_ref, sw_ref = oracle.quantize_rows_int8(w.numpy())
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    xs = f32(x) if rows is None else f32(x)[rows]
+    _, _, _, y_ref, D = oracle.w8a8_forward(xs, wq_ref, sw_ref, bias=None if bias is None else f32(bias))
+    yg = y if rows is None else y[torch.as_tensor(rows, device=y.device)]
+    return yg, y_ref, D
+
+
+def test_w8a8_workload_sampled_rows():
+    inp = workloads.workload_inputs("w8a8_perchannel")
+    rows = sorted(set([0, 127, 128, 1023] + list(np.random.default_rng(4).choice(1024, 28, replace=False))))
+    y, y_ref, D = _w8a8_case(inp, rows)
+    assert_close(y, y_ref, D, 4096, torch.float16, strict=True, label="w8a8 workload")
+
+
+@pytest.mark.parametrize("xdt", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(1, 64, 16), (37, 208, 45), (130, 512, 300)])
+def test_w8a8_variants(xdt, shape):
+    M, K, N = shape
+    inp = workloads.w8a8_inputs(M, K, N, x_dtype=ODT[xdt], bias=True, seed=M + K + N, outlier_frac=0.01)
+    y, y_ref, D = _w8a8_case(inp)
+    assert_close(y, y_ref, D, K, xdt, label=f"w8a8 {xdt} {shape}")
