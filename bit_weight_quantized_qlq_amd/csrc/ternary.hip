@@ -8,8 +8,9 @@
 // The prior-art Metal kernel re-reads every packed row once per batch row and
 // accumulates on the vector ALU.  Here each packed byte is read once for all
 // batch rows and the contraction runs on the matrix cores:
-//  * one block (4 waves) owns 16 packed rows = 64 output rows (4 fields);
-//    the waves split K, and an LDS reduction joins their partial sums;
+//  * one block (16 waves) owns 16 packed rows = 64 output rows (4 fields);
+//    the waves split K, issue all their loads before computing, and an
+//    LDS reduction joins their partial sums;
 //  * per 32-k step a lane loads 8 bytes (packed row l%16, 8 consecutive k) and
 //    turns field j of each 4-byte dword into two 16-bit float pairs with one
 //    shift and one and-or:  ((d >> 2j) & 0x00030003) | MAGIC = (OFF + c_k,
@@ -26,9 +27,10 @@ namespace qlq {
 
 namespace tern {
 constexpr int ROWS = 16;     // packed rows per block
-constexpr int WAVES = 4;
+constexpr int WAVES = 16;    // waves per block; they split K
 constexpr int THREADS = 64 * WAVES;
 constexpr int KS = 32;       // MFMA k-step
+constexpr int BATCH = 8;     // k-steps a wave loads before computing
 }  // namespace tern
 
 template <typename XT> struct TernT;
@@ -36,7 +38,7 @@ template <> struct TernT<bf16_t> {
   static constexpr uint32_t MAGIC = 0x43004300u;
   static constexpr uint32_t ONES = 0x3F803F80u;
   static constexpr float OFF = 128.0f;
-  static __device__ __forceinline__ f32x4_v mma(uint4 a, uint4 b, f32x4_v c) {
+  static __device__ __forceinline__ f32x4_v mma(u32x4_v a, u32x4_v b, f32x4_v c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a),
                                                    __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
   }
@@ -49,7 +51,7 @@ template <> struct TernT<f16_t> {
   static constexpr uint32_t MAGIC = 0x64006400u;
   static constexpr uint32_t ONES = 0x3C003C00u;
   static constexpr float OFF = 1024.0f;
-  static __device__ __forceinline__ f32x4_v mma(uint4 a, uint4 b, f32x4_v c) {
+  static __device__ __forceinline__ f32x4_v mma(u32x4_v a, u32x4_v b, f32x4_v c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_v, a),
                                                   __builtin_bit_cast(f16x8_v, b), c, 0, 0, 0);
   }
@@ -59,10 +61,13 @@ template <> struct TernT<f16_t> {
   }
 };
 
+// One block: 16 packed rows x 16 rows of x.  Wave w takes k-steps w, w+16, ...
+// in batches of BATCH: every load of a batch is issued before its MFMAs, so a
+// wave makes one memory round trip per batch (one in total for K <= 4096).
 template <typename XT>
 __global__ void __launch_bounds__(tern::THREADS)
-ternary_mfma_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ packed,
-                    int64_t R, const XT* __restrict__ wscale, int invert,
+ternary_mfma_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __restrict__ packed,
+                    int R, const XT* __restrict__ wscale, int invert,
                     const XT* __restrict__ bias, XT* __restrict__ y) {
   using namespace tern;
   using TT = TernT<XT>;
@@ -70,47 +75,51 @@ ternary_mfma_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint8_
   __shared__ float xsum_sh[WAVES][16];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * ROWS;
-  const int64_t m0 = (int64_t)blockIdx.y * 16;
-  const int64_t N = 4 * R;
-  int64_t prow = r0 + (lane & 15);
-  prow = prow < R ? prow : R - 1;
-  const int64_t mrow = m0 + (lane & 15);
+  const int r0 = blockIdx.x * ROWS;
+  const int m0 = blockIdx.y * 16;
+  const int N = 4 * R;
+  const int prow = min(r0 + (lane & 15), R - 1);
+  const int mrow = m0 + (lane & 15);
   const bool mvalid = mrow < M;
   const int kofs = (lane >> 4) * 8;
-  const uint8_t* wp = packed + prow * K + kofs;
-  const XT* xp = x + (mvalid ? mrow : 0) * K + kofs;
+  const uint8_t* wp = packed + (int64_t)prow * K + kofs;
+  const XT* xp = x + (int64_t)(mvalid ? mrow : 0) * K + kofs;
 
   f32x4_v P[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) P[j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   float xs = 0.0f;
 
-  const int64_t nsteps = K / KS;
-#pragma unroll 4
-  for (int64_t st = wid; st < nsteps; st += WAVES) {
-    const int64_t k0 = st * KS;
-    const uint2 wb = *reinterpret_cast<const uint2*>(wp + k0);
-    uint4 xv = make_uint4(0, 0, 0, 0);
-    if (mvalid) xv = *reinterpret_cast<const uint4*>(xp + k0);
-    // x pairs in the code order of a dword: (k0,k2), (k1,k3) per 4 k
-    uint4 a;
-    a.x = __builtin_amdgcn_perm(xv.y, xv.x, 0x05040100u);
-    a.y = __builtin_amdgcn_perm(xv.y, xv.x, 0x07060302u);
-    a.z = __builtin_amdgcn_perm(xv.w, xv.z, 0x05040100u);
-    a.w = __builtin_amdgcn_perm(xv.w, xv.z, 0x07060302u);
-    xs = TT::dot2(xv.x, TT::ONES, xs);
-    xs = TT::dot2(xv.y, TT::ONES, xs);
-    xs = TT::dot2(xv.z, TT::ONES, xs);
-    xs = TT::dot2(xv.w, TT::ONES, xs);
+  const int nsteps = K / KS;
+  for (int base = wid; base < nsteps; base += WAVES * BATCH) {
+    uint2 wb[BATCH];
+    u32x4_v xv[BATCH];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint4 b;
-      b.x = ((wb.x >> (2 * j)) & 0x00030003u) | TT::MAGIC;
-      b.y = ((wb.x >> (2 * j + 8)) & 0x00030003u) | TT::MAGIC;
-      b.z = ((wb.y >> (2 * j)) & 0x00030003u) | TT::MAGIC;
-      b.w = ((wb.y >> (2 * j + 8)) & 0x00030003u) | TT::MAGIC;
-      P[j] = TT::mma(a, b, P[j]);
+    for (int b = 0; b < BATCH; ++b) {
+      const int st = min(base + b * WAVES, nsteps - 1);  // clamped: extra steps are dropped below
+      wb[b] = *reinterpret_cast<const uint2*>(wp + st * KS);
+      xv[b] = *reinterpret_cast<const u32x4_v*>(xp + st * KS);
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      if (base + b * WAVES >= nsteps) break;
+      const u32x4_v v = mvalid ? xv[b] : u32x4_v{0, 0, 0, 0};
+      // x pairs in the code order of a dword: (k0,k2), (k1,k3) per 4 k
+      u32x4_v a;
+      a[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
+      a[1] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
+      a[2] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
+      a[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
+      xs = TT::dot2(v[3], TT::ONES, TT::dot2(v[2], TT::ONES, TT::dot2(v[1], TT::ONES, TT::dot2(v[0], TT::ONES, xs))));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4_v bq;
+        bq[0] = ((wb[b].x >> (2 * j)) & 0x00030003u) | TT::MAGIC;
+        bq[1] = ((wb[b].x >> (2 * j + 8)) & 0x00030003u) | TT::MAGIC;
+        bq[2] = ((wb[b].y >> (2 * j)) & 0x00030003u) | TT::MAGIC;
+        bq[3] = ((wb[b].y >> (2 * j + 8)) & 0x00030003u) | TT::MAGIC;
+        P[j] = TT::mma(a, bq, P[j]);
+      }
     }
   }
   // X[m] partial: lanes l, l+16, l+32, l+48 hold the same row
@@ -123,12 +132,10 @@ ternary_mfma_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint8_
   if (lane < 16) xsum_sh[wid][lane] = xs;
   __syncthreads();
 
-  float ws = Elem<XT>::load(wscale, 0);
+  const float ws = Elem<XT>::load(wscale, 0);
   const float sigma = invert ? __fdiv_rn(1.0f, ws) : ws;
-  // block outputs: 16 m x 4 fields x 16 packed rows = 1024, 4 per thread
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int o = tid + THREADS * it;       // o = ((j * 16) + mi) * 16 + ri  (ri fastest)
+  // block outputs: 16 m x 4 fields x 16 packed rows = 1024, one per thread
+  for (int o = tid; o < 1024; o += THREADS) {
     const int ri = o & 15, mi = (o >> 4) & 15, j = o >> 8;
     // D layout: lane = (mi / 4) * 16 + ri holds row mi at element mi % 4
     const int src_lane = (mi >> 2) * 16 + ri, e = mi & 3;
@@ -138,12 +145,12 @@ ternary_mfma_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint8_
       p += red[w][j][e][src_lane];
       X += xsum_sh[w][mi];
     }
-    const int64_t m = m0 + mi, r = r0 + ri;
+    const int m = m0 + mi, r = r0 + ri;
     if (m < M && r < R) {
-      const int64_t n = r + j * R;
+      const int n = r + j * R;
       float v = sigma * __fmaf_rn(-(TT::OFF + 1.0f), X, p);
       if (bias) v = v + Elem<XT>::load(bias, n);
-      Elem<XT>::store(y, m * N + n, v);
+      Elem<XT>::store(y, (int64_t)m * N + n, v);
     }
   }
 }
@@ -189,11 +196,12 @@ hipError_t launch_ternary_forward(const void* x, int x_dtype, int64_t M, int64_t
     return hipGetLastError();
   }
   dim3 grid((unsigned)cdiv(R, tern::ROWS), (unsigned)cdiv(M, 16)), block(tern::THREADS);
+  const int m = (int)M, k = (int)K, r = (int)R;
   if (x_dtype == BF16)
-    hipLaunchKernelGGL(ternary_mfma_kernel<bf16_t>, grid, block, 0, s, (const bf16_t*)x, M, K, packed, R,
+    hipLaunchKernelGGL(ternary_mfma_kernel<bf16_t>, grid, block, 0, s, (const bf16_t*)x, m, k, packed, r,
                        (const bf16_t*)weight_scale, invert, (const bf16_t*)bias, (bf16_t*)y);
   else
-    hipLaunchKernelGGL(ternary_mfma_kernel<f16_t>, grid, block, 0, s, (const f16_t*)x, M, K, packed, R,
+    hipLaunchKernelGGL(ternary_mfma_kernel<f16_t>, grid, block, 0, s, (const f16_t*)x, m, k, packed, r,
                        (const f16_t*)weight_scale, invert, (const f16_t*)bias, (f16_t*)y);
   return hipGetLastError();
 }
