@@ -48,8 +48,81 @@ __device__ __forceinline__ int floor_log2(float v) {  // v > 0, finite
 }
 
 // ------------------------------------------------------------------ pre-pass
-// Blocks [0, M): x row m -> x16 (k-order of the code pairs), e_m.
-// Blocks [M, M + ceil(N/256)): one thread per column n -> f_n.
+// Column exponents f_n: one thread per column n.
+template <int BITS, typename XT>
+__device__ __forceinline__ void column_exponent(const XT* __restrict__ scales, const XT* __restrict__ biases,
+                                                int n, int ng, int* __restrict__ wexp) {
+  constexpr float qmax = (float)((1 << BITS) - 1);
+  int f = -1000;
+  for (int g = 0; g < ng; ++g) {
+    const float s = Elem<XT>::load(scales, (int64_t)n * ng + g);
+    const float b = Elem<XT>::load(biases, (int64_t)n * ng + g);
+    const float top = fabsf(b) + qmax * fabsf(s);
+    if (s != 0.0f) f = max(f, floor_log2(fabsf(s)) + 10);
+    if (top != 0.0f) f = max(f, floor_log2(top) - 14);
+  }
+  wexp[n] = f == -1000 ? 0 : f;
+}
+
+// x16[m, k] for one row held by one wave: element k of block b (PER codes)
+// goes to position 2j or 2j+1 of the pair order (j, j + PER/2).  Lanes own
+// groups of 16 consecutive elements, interleaved across the wave (16-byte
+// coalesced loads and stores).  Blocks [0, ceil(M/4)) do rows (4 per block),
+// the remaining blocks do the column exponents.
+template <int BITS, typename XT, int EPT>
+__global__ void __launch_bounds__(256)
+gemm_prep_wave_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ scales,
+                      const XT* __restrict__ biases, int N, int G, f16_t* __restrict__ x16,
+                      int* __restrict__ xexp, int* __restrict__ wexp) {
+  constexpr int PER = 32 / BITS;
+  constexpr int HALF = PER / 2;
+  constexpr int G16 = EPT / 16;
+  const int row_blocks = (M + 3) / 4;
+  if ((int)blockIdx.x >= row_blocks) {
+    const int n = ((int)blockIdx.x - row_blocks) * 256 + threadIdx.x;
+    if (n < N) column_exponent<BITS, XT>(scales, biases, n, K / G, wexp);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const XT* xr = x + (int64_t)m * K;
+  float e[EPT];
+  bool in[G16];
+#pragma unroll
+  for (int g = 0; g < G16; ++g) {
+    const int k = (g * 64 + lane) * 16;
+    in[g] = k < K;
+    float t[16];
+    load16<XT>(xr + (in[g] ? k : 0), t);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[g * 16 + i] = in[g] ? t[i] : 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) amax = fmaxf(amax, fabsf(e[i]));
+  amax = wave_max_dpp(amax);
+  const int ex = amax > 0.0f ? floor_log2(amax) - 14 : 0;
+  if (lane == 0) xexp[m] = ex;
+  f16_t* out = x16 + (int64_t)m * K;
+#pragma unroll
+  for (int g = 0; g < G16; ++g) {
+    if (!in[g]) continue;
+    uint32_t w[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {  // output pair p = positions 2p, 2p+1 of the 16
+      const int lo = (2 * p) / PER * PER + p % HALF;  // (j, j + PER/2) within block
+      const int i0 = PER >= 16 ? p : lo, i1 = PER >= 16 ? p + HALF : lo + HALF;
+      const f16x2_v h = {(f16_t)ldexpf(e[g * 16 + i0], -ex), (f16_t)ldexpf(e[g * 16 + i1], -ex)};
+      w[p] = __builtin_bit_cast(uint32_t, h);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(out + (g * 64 + lane) * 16);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// General K: one block per row (rows), then the column exponents.
 template <int BITS, typename XT>
 __global__ void __launch_bounds__(256)
 gemm_prep_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ scales,
@@ -60,18 +133,7 @@ gemm_prep_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ 
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= M) {
     const int n = ((int)blockIdx.x - M) * 256 + tid;
-    if (n >= N) return;
-    const int ng = K / G;
-    constexpr float qmax = (float)((1 << BITS) - 1);
-    int f = -1000;
-    for (int g = 0; g < ng; ++g) {
-      const float s = Elem<XT>::load(scales, (int64_t)n * ng + g);
-      const float b = Elem<XT>::load(biases, (int64_t)n * ng + g);
-      const float top = fabsf(b) + qmax * fabsf(s);
-      if (s != 0.0f) f = max(f, floor_log2(fabsf(s)) + 10);
-      if (top != 0.0f) f = max(f, floor_log2(top) - 14);
-    }
-    wexp[n] = f == -1000 ? 0 : f;
+    if (n < N) column_exponent<BITS, XT>(scales, biases, n, K / G, wexp);
     return;
   }
   __shared__ float red[4];
@@ -307,8 +369,19 @@ static hipError_t gemm_launch(const void* x, int64_t M, int64_t K, const uint32_
   int* xexp = (int*)((char*)ws + x16b);
   int* wexp = (int*)((char*)ws + x16b + (((size_t)M * 4 + 255) & ~(size_t)255));
   const int m = (int)M, n = (int)N, k = (int)K;
-  hipLaunchKernelGGL((gemm_prep_kernel<BITS, XT>), dim3((unsigned)(M + cdiv(N, 256))), dim3(256), 0, s,
-                     (const XT*)x, m, k, (const XT*)scales, (const XT*)biases, n, G, x16, xexp, wexp);
+  if (K <= 64 * 64) {
+    const unsigned blocks = (unsigned)(cdiv(M, 4) + cdiv(N, 256));
+#define QLQ_PREP(EPT_)                                                                                  \
+  hipLaunchKernelGGL((gemm_prep_wave_kernel<BITS, XT, EPT_>), dim3(blocks), dim3(256), 0, s, (const XT*)x, m, \
+                     k, (const XT*)scales, (const XT*)biases, n, G, x16, xexp, wexp)
+    if (K <= 64 * 16) QLQ_PREP(16);
+    else if (K <= 64 * 32) QLQ_PREP(32);
+    else QLQ_PREP(64);
+#undef QLQ_PREP
+  } else {
+    hipLaunchKernelGGL((gemm_prep_kernel<BITS, XT>), dim3((unsigned)(M + cdiv(N, 256))), dim3(256), 0, s,
+                       (const XT*)x, m, k, (const XT*)scales, (const XT*)biases, n, G, x16, xexp, wexp);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tiles = cdiv(M, gemm::BM) * cdiv(N, gemm::BN);

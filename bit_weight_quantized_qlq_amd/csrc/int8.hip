@@ -9,9 +9,11 @@
 // Epilogue: y = fp32(c) * sa[m] * sb[n] (+ bias[n]), rounded once to the
 // output dtype.
 //
-// Tiling: 256 threads (2x2 waves), block tile 128x128, k-iteration 128,
-// wave tile 64x64 = 2x2 MFMA 32x32x32 tiles, LDS double buffer fed from two
-// register stages, XCD-aware tile order.
+// Tiling: block tile 128x128, k-iteration 128, 8 waves: 4 sub-tiles of 64x64
+// (2x2 MFMA 32x32x32 tiles) times 2 halves of each k-iteration's k-steps, so
+// two waves share each SIMD while one block covers a CU; the halves are summed
+// through LDS at the end.  LDS double buffer fed from two register stages,
+// XCD-aware tile order.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile.hpp"
@@ -20,9 +22,10 @@ namespace qlq {
 
 namespace i8 {
 constexpr int BM = 128, BN = 128, BK = 128, KS = 32;  // KS: MFMA k-step
-constexpr int THREADS = 256;
+constexpr int WAVES = 8;   // 4 sub-tiles x 2 halves of each k-iteration
+constexpr int THREADS = 64 * WAVES;
 constexpr int LDS_STRIDE = BK + 16;  // bytes per LDS row (16-byte pad)
-constexpr int U4_T = BM * BK / 16 / THREADS;  // 4 uint4 per thread per operand
+constexpr int U4_T = BM * BK / 16 / THREADS;  // 16-byte loads per thread per operand
 }  // namespace i8
 
 typedef __attribute__((ext_vector_type(16))) int i32x16_v;
@@ -47,11 +50,16 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
                  const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
                  void* __restrict__ out) {
   using namespace i8;
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * LDS_STRIDE];
+  // one LDS allocation: two A and two B tile buffers during the K loop, then
+  // the 64 KiB of int32 partial sums that join the two k-halves
+  __shared__ __attribute__((aligned(16))) int8_t smem[2 * (BM + BN) * LDS_STRIDE];
+  static_assert(2 * (BM + BN) * LDS_STRIDE >= 4 * 64 * 64 * 4, "reduction area fits");
+  int8_t (*As)[BM * LDS_STRIDE] = reinterpret_cast<int8_t (*)[BM * LDS_STRIDE]>(smem);
+  int8_t (*Bs)[BN * LDS_STRIDE] = reinterpret_cast<int8_t (*)[BN * LDS_STRIDE]>(smem + 2 * BM * LDS_STRIDE);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wq = wid & 3, kh = wid >> 2;  // 64x64 sub-tile, half of the k-steps
+  const int wm = wq >> 1, wn = wq & 1;
   int tm, tn;
   tile_coords<8>(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   const int m_blk = tm * BM, n_blk = tn * BN;
@@ -105,7 +113,7 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
   const int kofs = (lane >> 5) * 16;
 #define QLQ_COMPUTE(BUF)                                                                               \
   do {                                                                                                 \
-    _Pragma("unroll") for (int ks = 0; ks < BK; ks += KS) {                                            \
+    _Pragma("unroll") for (int ks = kh * (BK / 2); ks < kh * (BK / 2) + BK / 2; ks += KS) {            \
       u32x4_v af_[2], bf_[2];                                                                          \
       _Pragma("unroll") for (int i = 0; i < 2; ++i)                                                    \
           af_[i] = *reinterpret_cast<const u32x4_v*>(&As[BUF][(a_row + 32 * i) * LDS_STRIDE + ks + kofs]); \
@@ -140,6 +148,27 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
 #undef QLQ_LOAD
 #undef QLQ_STORE
 #undef QLQ_COMPUTE
+
+  // ---- join the two k-halves: waves 4-7 park their sums in LDS (the tile
+  // buffers are free now), waves 0-3 add them and run the epilogue
+  int32_t* red = reinterpret_cast<int32_t*>(smem);  // 4 sub-tiles x 64 values x 64 lanes
+  __syncthreads();
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red[(wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane] = acc[i][j][e];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] += red[(wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane];
 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {

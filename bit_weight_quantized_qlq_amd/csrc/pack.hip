@@ -8,8 +8,10 @@
 //
 // Every floating-point step that decides an integer is a single IEEE fp32
 // operation with round-to-nearest-even (__fsub_rn, __fdiv_rn, rintf), so the
-// codes equal those of an fp32 reference bit for bit.  These kernels are off
-// the timed path; they favour plain indexing over peak bandwidth.
+// codes equal those of an fp32 reference bit for bit.  The packing kernels
+// run offline and favour plain indexing; the row int8 quantizer also
+// quantizes activations on the W8A8 forward path and is written for
+// bandwidth (one wave per row, the row held in registers).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -205,39 +207,6 @@ hipError_t launch_ternary_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* p
 // Pass 2: q = clamp(rint(v / s), -128, 127) with s = a / 127 (1 if 0).
 // Each thread handles 16 consecutive elements per step (K % 16 == 0).
 template <typename T>
-__device__ __forceinline__ void load16(const T* p, float (&v)[16]);
-template <>
-__device__ __forceinline__ void load16<float>(const float* p, float (&v)[16]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float4 f = reinterpret_cast<const float4*>(p)[i];
-    v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
-  }
-}
-template <>
-__device__ __forceinline__ void load16<bf16_t>(const bf16_t* p, float (&v)[16]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    uint4 u = reinterpret_cast<const uint4*>(p)[i];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-    }
-  }
-}
-template <>
-__device__ __forceinline__ void load16<f16_t>(const f16_t* p, float (&v)[16]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    f16x8_v h = reinterpret_cast<const f16x8_v*>(p)[i];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[8 * i + j] = (float)h[j];
-  }
-}
-
-template <typename T>
 __global__ void __launch_bounds__(256)
 quantize_rows_int8_kernel(const T* __restrict__ v, int64_t K, int8_t* __restrict__ q,
                           float* __restrict__ scale) {
@@ -281,19 +250,76 @@ quantize_rows_int8_kernel(const T* __restrict__ v, int64_t K, int8_t* __restrict
   }
 }
 
+// Register-resident variant for K <= 64 * EPT: one wave per row, each lane
+// keeps its EPT consecutive elements (16-byte loads) in registers, so the row
+// is read once; max by DPP; no block barrier.
+template <typename T, int EPT>
+__global__ void __launch_bounds__(256)
+quantize_rows_int8_wave_kernel(const T* __restrict__ v, int R, int K, int8_t* __restrict__ q,
+                               float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const T* vr = v + (int64_t)row * K;
+  constexpr int G16 = EPT / 16;  // groups of 16 elements per lane
+  float e[EPT];
+  bool in[G16];
+#pragma unroll
+  for (int g = 0; g < G16; ++g) {
+    const int k = (g * 64 + lane) * 16;  // lanes interleave 16-element groups: coalesced
+    in[g] = k < K;
+    float t[16];
+    load16<T>(vr + (in[g] ? k : 0), t);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[g * 16 + i] = in[g] ? t[i] : 0.0f;
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) a = fmaxf(a, fabsf(e[i]));
+  a = wave_max_dpp(a);
+  float s = __fdiv_rn(a, 127.0f);
+  if (s == 0.0f) s = 1.0f;
+  if (lane == 0) scale[row] = s;
+#pragma unroll
+  for (int g = 0; g < G16; ++g) {
+    if (!in[g]) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float r = rintf(__fdiv_rn(e[g * 16 + 4 * i + j], s));
+        r = fminf(fmaxf(r, -128.0f), 127.0f);
+        word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
+      }
+      w[i] = word;
+    }
+    *reinterpret_cast<uint4*>(q + (int64_t)row * K + (g * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+template <typename T>
+static void quant_rows_launch(const void* v, int64_t R, int64_t K, int8_t* q, float* scale, hipStream_t s) {
+  if (K <= 64 * 64) {
+    dim3 grid((unsigned)cdiv(R, 4)), block(256);
+    if (K <= 64 * 16)
+      hipLaunchKernelGGL((quantize_rows_int8_wave_kernel<T, 16>), grid, block, 0, s, (const T*)v, (int)R, (int)K, q, scale);
+    else if (K <= 64 * 32)
+      hipLaunchKernelGGL((quantize_rows_int8_wave_kernel<T, 32>), grid, block, 0, s, (const T*)v, (int)R, (int)K, q, scale);
+    else
+      hipLaunchKernelGGL((quantize_rows_int8_wave_kernel<T, 64>), grid, block, 0, s, (const T*)v, (int)R, (int)K, q, scale);
+  } else {
+    hipLaunchKernelGGL(quantize_rows_int8_kernel<T>, dim3((unsigned)R), dim3(256), 0, s, (const T*)v, K, q, scale);
+  }
+}
+
 hipError_t launch_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_t K, int8_t* q,
                                      float* scale, hipStream_t s) {
-  dim3 grid((unsigned)R), block(256);
   switch (v_dtype) {
-    case F32:
-      hipLaunchKernelGGL(quantize_rows_int8_kernel<float>, grid, block, 0, s, (const float*)v, K, q, scale);
-      break;
-    case BF16:
-      hipLaunchKernelGGL(quantize_rows_int8_kernel<bf16_t>, grid, block, 0, s, (const bf16_t*)v, K, q, scale);
-      break;
-    default:
-      hipLaunchKernelGGL(quantize_rows_int8_kernel<f16_t>, grid, block, 0, s, (const f16_t*)v, K, q, scale);
-      break;
+    case F32: quant_rows_launch<float>(v, R, K, q, scale, s); break;
+    case BF16: quant_rows_launch<bf16_t>(v, R, K, q, scale, s); break;
+    default: quant_rows_launch<f16_t>(v, R, K, q, scale, s); break;
   }
   return hipGetLastError();
 }

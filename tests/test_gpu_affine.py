@@ -134,7 +134,7 @@ def test_forward_prefill_full_sampled_rows():
 SHAPES = [  # (M, K, N, bits, G)
     (1, 416, 200, 4, 32), (2, 448, 130, 4, 64), (3, 640, 77, 4, 128), (5, 448, 64, 2, 64),
     (8, 384, 129, 8, 128), (9, 416, 200, 4, 32), (17, 448, 250, 2, 64), (33, 640, 131, 4, 128),
-    (130, 384, 257, 8, 64), (1, 4096, 96, 4, 64), (20, 416, 72, 2, 32),
+    (130, 384, 257, 8, 64), (1, 4096, 96, 4, 64), (20, 416, 72, 2, 32), (40, 4160, 72, 4, 64),
 ]
 
 

@@ -14,8 +14,9 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("vdt", [torch.float16, torch.bfloat16, torch.float32])
-def test_quantize_rows_bitexact(vdt):
-    inp = workloads.w8a8_inputs(97, 4096 + 64, 8, x_dtype=ODT[vdt], seed=21)
+@pytest.mark.parametrize("K", [16, 1008, 2048, 4096, 4096 + 64])
+def test_quantize_rows_bitexact(vdt, K):
+    inp = workloads.w8a8_inputs(97, K, 8, x_dtype=ODT[vdt], seed=21 + K)
     v = inp["x"]
     v[5] = 0  # a zero row takes scale 1
     q, s = qlq.qlq_quantize_rows_int8(v.to(dev()))
