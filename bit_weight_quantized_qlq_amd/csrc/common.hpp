@@ -141,4 +141,16 @@ __device__ __forceinline__ void load16<f16_t>(const f16_t* p, float (&v)[16]) {
 
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Raw buffer access (stride 0): the hardware checks every byte offset against
+// the descriptor's size and returns zero for reads past it.  kOutOfRange is an
+// offset past any buffer made here (sizes stay below 2^31 bytes).  0x00020000
+// is the gfx9-family word 3 of a raw buffer descriptor (32-bit data format).
+constexpr int kOutOfRange = (int)0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_v load_b128(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
 }  // namespace qlq

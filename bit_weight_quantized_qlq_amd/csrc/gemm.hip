@@ -311,16 +311,25 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
   QLQ_LOAD(1, min(1, last));
   QLQ_STORE(0, 0);
   QLQ_LOAD(0, min(2, last));
-  for (int it = 0; it < nk; it += 2) {
+  // The loop body holds a whole even/odd pair with no exit in between: an
+  // exit there lets the compiler sink one stage's loads down to their first
+  // use, which removes the prefetch.  An odd last tile is finished after it.
+  int it = 0;
+  for (; it + 1 < nk; it += 2) {
+    // even step: compute buffer 0; stage 1 (tile it+1) -> buffer 1
     __syncthreads();
     QLQ_STORE(1, 1);
     QLQ_LOAD(1, min(it + 3, last));
     QLQ_COMPUTE(0);
-    if (it + 1 >= nk) break;
+    // odd step: compute buffer 1; stage 0 (tile it+2) -> buffer 0
     __syncthreads();
     QLQ_STORE(0, 0);
     QLQ_LOAD(0, min(it + 4, last));
     QLQ_COMPUTE(1);
+  }
+  if (it < nk) {  // odd nk: buffer 0 holds the last tile
+    __syncthreads();
+    QLQ_COMPUTE(0);
   }
 #undef QLQ_LOAD
 #undef QLQ_STORE

@@ -9,11 +9,18 @@
 // Epilogue: y = fp32(c) * sa[m] * sb[n] (+ bias[n]), rounded once to the
 // output dtype.
 //
-// Tiling: block tile 128x128, k-iteration 128, 8 waves: 4 sub-tiles of 64x64
+// Tiling: block tile 128x128, k-iteration BK (256), 8 waves: 4 sub-tiles of 64x64
 // (2x2 MFMA 32x32x32 tiles) times 2 halves of each k-iteration's k-steps, so
 // two waves share each SIMD while one block covers a CU; the halves are summed
-// through LDS at the end.  LDS double buffer fed from two register stages,
-// XCD-aware tile order.
+// through LDS at the end.  XCD-aware tile order.
+//
+// Operand tiles go from global memory straight into a ring of STAGES LDS
+// buffers (buffer loads with the LDS-destination bit: no register staging,
+// no LDS store instructions).  A load whose offset lies past the buffer's
+// size writes zeros, which covers rows past M / N and k past K.  Each
+// 128-byte LDS row holds its eight 16-byte k-chunks in swizzled slots (chunk
+// c of row r at slot c ^ swz(r)), so the fragment reads of 8 or 16 lanes
+// (consecutive rows, same chunk) fall on distinct banks.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile.hpp"
@@ -21,11 +28,26 @@
 namespace qlq {
 
 namespace i8 {
-constexpr int BM = 128, BN = 128, BK = 128, KS = 32;  // KS: MFMA k-step
+constexpr int BM = 128, BN = 128, KS = 32;  // KS: MFMA k-step
 constexpr int WAVES = 8;   // 4 sub-tiles x 2 halves of each k-iteration
 constexpr int THREADS = 64 * WAVES;
-constexpr int LDS_STRIDE = BK + 16;  // bytes per LDS row (16-byte pad)
-constexpr int U4_T = BM * BK / 16 / THREADS;  // 16-byte loads per thread per operand
+constexpr int ROWS_W = BM / WAVES;  // tile rows each wave loads (per operand)
+// k-iteration BK bytes, ring of STAGES slots
+template <int BK, int STAGES> struct Cfg {
+  static constexpr int CPR = BK / 16;           // 16-byte chunks per LDS row
+  static constexpr int RPI = 1024 / BK;         // rows one wave-wide load fills
+  static constexpr int TILE = BM * BK;          // bytes of one operand tile (BM == BN)
+  static constexpr int STAGE = 2 * TILE;        // A tile then B tile
+  static constexpr int LPW = ROWS_W / RPI;      // loads per thread per operand tile
+  static constexpr int LPT = 2 * LPW;           // loads per thread per k-iteration
+  static constexpr int QN = BK / KS / 2;        // k-steps per wave per k-iteration
+  static constexpr int VMCNT = (STAGES - 2) * LPT;  // loads allowed outstanding at the wait
+  static_assert(BM == BN && (BK == 128 || BK == 256) && ROWS_W % RPI == 0, "tile shape");
+  static_assert(STAGES >= 2 && VMCNT < 64, "ring depth");
+  // slot of chunk c in row r is c ^ swz(r): 8 or 16 consecutive rows read at
+  // one chunk land on distinct banks
+  static __device__ __forceinline__ int swz(int r) { return BK == 128 ? ((r + (r >> 3)) & 7) : (r & 15); }
+};
 }  // namespace i8
 
 typedef __attribute__((ext_vector_type(16))) int i32x16_v;
@@ -37,25 +59,25 @@ __device__ __forceinline__ i32x16_v mma_i8(u32x4_v a, u32x4_v b, i32x16_v c) {
                                                 c, 0, 0, 0);
 }
 
-// Pipeline (one barrier per k-iteration): register stage (it+1)%2 holds the
-// tile of iteration it+1, loaded two iterations earlier.  Step `it`:
-//   barrier; store regs[(it+1)%2] -> LDS[(it+1)%2]; load tile it+3 into the
-//   freed registers; compute tile it from LDS[it%2].
-// Two tiles stay in flight while a third is computed.  Rows past M / N and
-// k past K are read from clamped addresses and zeroed with a select, so the
-// loop has no branches.
-template <int OUT>
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Pipeline (one barrier per k-iteration).  Before iteration `it`, tiles
+// it .. it+STAGES-2 are in flight to their ring slots.  Iteration it: wait
+// until this thread's loads of tile it have landed, barrier (every thread's
+// have, and every wave has finished reading slot (it-1) % STAGES), issue the
+// loads of tile it+STAGES-1 into that slot, compute tile it.  Tiles past the
+// last one load as zeros and are never computed.
+template <int OUT, int BK, int STAGES>
 __global__ void __launch_bounds__(i8::THREADS, 1)
 int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int M, int N, int K,
                  const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
                  void* __restrict__ out) {
   using namespace i8;
-  // one LDS allocation: two A and two B tile buffers during the K loop, then
-  // the 64 KiB of int32 partial sums that join the two k-halves
-  __shared__ __attribute__((aligned(16))) int8_t smem[2 * (BM + BN) * LDS_STRIDE];
-  static_assert(2 * (BM + BN) * LDS_STRIDE >= 4 * 64 * 64 * 4, "reduction area fits");
-  int8_t (*As)[BM * LDS_STRIDE] = reinterpret_cast<int8_t (*)[BM * LDS_STRIDE]>(smem);
-  int8_t (*Bs)[BN * LDS_STRIDE] = reinterpret_cast<int8_t (*)[BN * LDS_STRIDE]>(smem + 2 * BM * LDS_STRIDE);
+  using C = Cfg<BK, STAGES>;
+  // the ring during the K loop, then the 64 KiB of int32 partial sums that
+  // join the two k-halves
+  __shared__ __attribute__((aligned(16))) int8_t smem[STAGES * C::STAGE];
+  static_assert(STAGES * C::STAGE >= 4 * 64 * 64 * 4, "reduction area fits");
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wq = wid & 3, kh = wid >> 2;  // 64x64 sub-tile, half of the k-steps
@@ -65,43 +87,41 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
   const int m_blk = tm * BM, n_blk = tn * BN;
   const int nk = (K + BK - 1) / BK;
 
-  // per-thread load coordinates (fixed across k-iterations)
-  const int8_t* ap[U4_T];
-  const int8_t* bp[U4_T];
-  int lofs[U4_T], kc[U4_T];
+  const int rows_a = min(BM, M - m_blk), rows_b = min(BN, N - n_blk);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(a + (int64_t)m_blk * K, rows_a * K);
+  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(b + (int64_t)n_blk * K, rows_b * K);
+  // load j of this thread: row wid*ROWS_W + RPI*j + lane/CPR of both tiles,
+  // chunk (lane % CPR) ^ swz(row), i.e. LDS slot lane % CPR
+  int voff[C::LPW], kc[C::LPW];
 #pragma unroll
-  for (int i = 0; i < U4_T; ++i) {
-    const int idx = tid + THREADS * i, r = idx / (BK / 16), c = idx % (BK / 16);
-    const int gm = min(m_blk + r, M - 1), gn = min(n_blk + r, N - 1);
-    ap[i] = a + (int64_t)gm * K + c * 16;
-    bp[i] = b + (int64_t)gn * K + c * 16;
-    lofs[i] = r * LDS_STRIDE + c * 16;
-    kc[i] = c * 16;
+  for (int j = 0; j < C::LPW; ++j) {
+    const int r = wid * ROWS_W + C::RPI * j + lane / C::CPR, c = (lane % C::CPR) ^ C::swz(r);
+    voff[j] = r * K + c * 16;
+    kc[j] = c * 16;
   }
-  u32x4_v ra0[U4_T], ra1[U4_T], rb0[U4_T], rb1[U4_T];
-  // Stage operations as macros: literal register-array indices only.
-  int k0s0 = 0, k0s1 = 0;  // k offset of the tile each register stage holds
-  // Stage operations as macros: literal register-array indices only.  The
-  // load stage only issues loads (any use of the loaded registers would make
-  // the compiler wait for them right there); the K-tail zeroing happens when
-  // the stage is written to LDS.
-#define QLQ_LOAD(ST, IT)                                                   \
-  do {                                                                     \
-    k0s##ST = (IT) * BK;                                                   \
-    _Pragma("unroll") for (int i = 0; i < U4_T; ++i) {                     \
-      const int kk_ = k0s##ST + kc[i] < K ? k0s##ST : 0;                   \
-      ra##ST[i] = *reinterpret_cast<const u32x4_v*>(ap[i] + kk_);          \
-      rb##ST[i] = *reinterpret_cast<const u32x4_v*>(bp[i] + kk_);          \
-    }                                                                      \
+#define QLQ_ISSUE(T)                                                                            \
+  do {                                                                                          \
+    const int k0_ = (T) * BK;                                                                   \
+    int8_t* dst_ = smem + ((T) % STAGES) * C::STAGE + wid * ROWS_W * BK;                        \
+    _Pragma("unroll") for (int j = 0; j < C::LPW; ++j) {                                        \
+      const int o_ = k0_ + kc[j] < K ? voff[j] + k0_ : kOutOfRange;                             \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(dst_ + 1024 * j), 16, o_, 0, 0, 0);           \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(dst_ + C::TILE + 1024 * j), 16, o_, 0, 0, 0); \
+    }                                                                                           \
   } while (0)
-#define QLQ_STORE(ST, BUF)                                                 \
-  do {                                                                     \
-    _Pragma("unroll") for (int i = 0; i < U4_T; ++i) {                     \
-      const bool in_ = k0s##ST + kc[i] < K;                                \
-      *reinterpret_cast<u32x4_v*>(&As[BUF][lofs[i]]) = in_ ? ra##ST[i] : u32x4_v{0, 0, 0, 0}; \
-      *reinterpret_cast<u32x4_v*>(&Bs[BUF][lofs[i]]) = in_ ? rb##ST[i] : u32x4_v{0, 0, 0, 0}; \
-    }                                                                      \
-  } while (0)
+
+  // fragment offsets inside a stage: [operand i/j][k-step q]
+  int aoff[2][C::QN], boff[2][C::QN];
+#pragma unroll
+  for (int q = 0; q < C::QN; ++q) {
+    const int c = (kh * C::QN + q) * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ra = wm * 64 + 32 * i + (lane & 31), rb = wn * 64 + 32 * i + (lane & 31);
+      aoff[i][q] = ra * BK + (c ^ C::swz(ra)) * 16;
+      boff[i][q] = C::TILE + rb * BK + (c ^ C::swz(rb)) * 16;
+    }
+  }
 
   i32x16_v acc[2][2];
 #pragma unroll
@@ -109,45 +129,32 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = i32x16_v{};
 
-  const int a_row = wm * 64 + (lane & 31), b_row = wn * 64 + (lane & 31);
-  const int kofs = (lane >> 5) * 16;
-#define QLQ_COMPUTE(BUF)                                                                               \
-  do {                                                                                                 \
-    _Pragma("unroll") for (int ks = kh * (BK / 2); ks < kh * (BK / 2) + BK / 2; ks += KS) {            \
-      u32x4_v af_[2], bf_[2];                                                                          \
-      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                                    \
-          af_[i] = *reinterpret_cast<const u32x4_v*>(&As[BUF][(a_row + 32 * i) * LDS_STRIDE + ks + kofs]); \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                    \
-          bf_[j] = *reinterpret_cast<const u32x4_v*>(&Bs[BUF][(b_row + 32 * j) * LDS_STRIDE + ks + kofs]); \
-      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                                    \
-          _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] = mma_i8(af_[i], bf_[j], acc[i][j]);   \
-    }                                                                                                  \
-  } while (0)
-
-  // Loads past the last tile re-read the last tile (clamped index) and the
-  // matching stores fill the idle buffer: both are harmless and keep the loop
-  // body free of conditional register writes.
-  const int last = nk - 1;
-  QLQ_LOAD(0, 0);
-  QLQ_LOAD(1, min(1, last));
-  QLQ_STORE(0, 0);
-  QLQ_LOAD(0, min(2, last));
-  for (int it = 0; it < nk; it += 2) {
-    // even step: compute buffer 0; stage 1 (tile it+1) -> buffer 1
-    __syncthreads();
-    QLQ_STORE(1, 1);
-    QLQ_LOAD(1, min(it + 3, last));
-    QLQ_COMPUTE(0);
-    if (it + 1 >= nk) break;
-    // odd step: compute buffer 1; stage 0 (tile it+2) -> buffer 0
-    __syncthreads();
-    QLQ_STORE(0, 0);
-    QLQ_LOAD(0, min(it + 4, last));
-    QLQ_COMPUTE(1);
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t) QLQ_ISSUE(t);
+  for (int it = 0; it < nk; ++it) {
+    // this thread's loads of tile it are done when at most the later
+    // STAGES-2 tiles' loads are outstanding; then the barrier
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(C::VMCNT) : "memory");
+    QLQ_ISSUE(it + STAGES - 1);
+    const int8_t* st_ = smem + (it % STAGES) * C::STAGE;
+    u32x4_v af[2][C::QN], bf[2][C::QN];
+#pragma unroll
+    for (int q = 0; q < C::QN; ++q)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i][q] = *reinterpret_cast<const u32x4_v*>(st_ + aoff[i][q]);
+        bf[i][q] = *reinterpret_cast<const u32x4_v*>(st_ + boff[i][q]);
+      }
+#pragma unroll
+    for (int q = 0; q < C::QN; ++q)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mma_i8(af[i][q], bf[j][q], acc[i][j]);
   }
-#undef QLQ_LOAD
-#undef QLQ_STORE
-#undef QLQ_COMPUTE
+#undef QLQ_ISSUE
+  // the zero tiles issued past the end may still be landing in the ring
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- join the two k-halves: waves 4-7 park their sums in LDS (the tile
   // buffers are free now), waves 0-3 add them and run the epilogue
@@ -198,19 +205,29 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
   }
 }
 
-hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K,
-                            const float* sa, const float* sb, const void* bias, int out_dtype,
-                            void* out, hipStream_t s) {
+template <int BK, int STAGES>
+hipError_t launch_int8_gemm_cfg(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K,
+                                const float* sa, const float* sb, const void* bias, int out_dtype,
+                                void* out, hipStream_t s) {
   const int64_t tiles = cdiv(M, i8::BM) * cdiv(N, i8::BN);
   dim3 grid((unsigned)tiles), block(i8::THREADS);
   const int m = (int)M, n = (int)N, k = (int)K;
   if (out_dtype < 0)
-    hipLaunchKernelGGL(int8_gemm_kernel<0>, grid, block, 0, s, a, b, m, n, k, sa, sb, bias, out);
+    hipLaunchKernelGGL((int8_gemm_kernel<0, BK, STAGES>), grid, block, 0, s, a, b, m, n, k, sa, sb, bias, out);
   else if (out_dtype == F16)
-    hipLaunchKernelGGL(int8_gemm_kernel<1>, grid, block, 0, s, a, b, m, n, k, sa, sb, bias, out);
+    hipLaunchKernelGGL((int8_gemm_kernel<1, BK, STAGES>), grid, block, 0, s, a, b, m, n, k, sa, sb, bias, out);
   else
-    hipLaunchKernelGGL(int8_gemm_kernel<2>, grid, block, 0, s, a, b, m, n, k, sa, sb, bias, out);
+    hipLaunchKernelGGL((int8_gemm_kernel<2, BK, STAGES>), grid, block, 0, s, a, b, m, n, k, sa, sb, bias, out);
   return hipGetLastError();
+}
+
+hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K,
+                            const float* sa, const float* sb, const void* bias, int out_dtype,
+                            void* out, hipStream_t s) {
+  // 256-byte k-iterations, double-buffered: fewer barriers per MFMA than
+  // 128-byte iterations in a deeper ring (measured faster on 1024x4096x4096
+  // and 2048x11008x4096)
+  return launch_int8_gemm_cfg<256, 2>(a, b, M, N, K, sa, sb, bias, out_dtype, out, s);
 }
 
 }  // namespace qlq

@@ -55,6 +55,15 @@ def test_forward_large_k_ragged_rows():
     assert_close(y, y_ref, D, K, torch.bfloat16, label="ternary K=4096")
 
 
+def test_forward_many_blocks_ragged():
+    # a grid of 129 x 4 blocks with a ragged last block in both directions
+    # (R = 2053 packed rows, M = 61)
+    N, K, M = 4 * 2053, 128, 61
+    inp = workloads.ternary_inputs(M, K, N, seed=12, bias=True)
+    y, y_ref, D = _case(inp, N)
+    assert_close(y, y_ref, D, K, torch.bfloat16, label="ternary wide blocks")
+
+
 def test_pack_rejects_out_of_set():
     t = torch.zeros(8, 32, dtype=torch.int8, device=dev())
     t[3, 4] = 2
