@@ -91,8 +91,12 @@ int check_affine_shape(int64_t N, int64_t K, int bits, int G) {
 }
 
 // The GEMM path takes 16-bit x with K a multiple of its 64-wide k-iteration.
-bool takes_gemm(int64_t M, int64_t K, int x_dtype) {
-  return x_dtype != QLQ_F32 && M > g_skinny_max_m && K % 64 == 0;
+// The prefill GEMM addresses its operands through 32-bit buffer offsets: a
+// 128-row tile of x16 (256 K bytes) and the (s', b') table (4 (K/G) N bytes)
+// must stay below 2^31 bytes; other shapes take the skinny kernel.
+bool takes_gemm(int64_t M, int64_t K, int64_t N, int G, int x_dtype) {
+  return x_dtype != QLQ_F32 && M > g_skinny_max_m && K % 64 == 0 && K * 256 < kMaxDim &&
+         (K / G) * ((N + 3) & ~(int64_t)3) * 4 < kMaxDim;
 }
 
 // one-shot device int flag for the synchronising pack calls
@@ -179,8 +183,8 @@ QLQ_API size_t qlq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int bi
                                          int x_dtype) {
   (void)bits;
   if (M <= 0 || K <= 0 || N <= 0 || group_size <= 0 || K % group_size) return 0;
-  if (!takes_gemm(M, K, x_dtype)) return 0;
-  return qlq::affine_gemm_workspace(M, K, N);
+  if (!takes_gemm(M, K, N, group_size, x_dtype)) return 0;
+  return qlq::affine_gemm_workspace(M, K, N, group_size);
 }
 
 QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
@@ -196,9 +200,9 @@ QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
   QLQ_REQUIRE(aligned(x, 16) && aligned(packed, 16), QLQ_ERR_ALIGNMENT, "x / packed not 16-byte aligned");
   QLQ_REQUIRE(aligned(scales, es) && aligned(biases, es) && aligned(y, es) && (!bias || aligned(bias, es)),
               QLQ_ERR_ALIGNMENT, "misaligned scales / biases / bias / y");
-  const bool gemm = takes_gemm(M, K, x_dtype);
+  const bool gemm = takes_gemm(M, K, N, group_size, x_dtype);
   if (gemm) {
-    const size_t need = qlq::affine_gemm_workspace(M, K, N);
+    const size_t need = qlq::affine_gemm_workspace(M, K, N, group_size);
     QLQ_REQUIRE(workspace && workspace_bytes >= need, QLQ_ERR_WORKSPACE,
                 "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
     QLQ_REQUIRE(aligned(workspace, 256), QLQ_ERR_ALIGNMENT, "workspace not 256-byte aligned");

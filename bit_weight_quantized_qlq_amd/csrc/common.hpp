@@ -153,4 +153,24 @@ __device__ __forceinline__ u32x4_v load_b128(__amdgpu_buffer_rsrc_t r, int off) 
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// dst + 16 i (dst wave-uniform); an out-of-range offset writes zeros.
+__device__ __forceinline__ void load_lds_b128(__amdgpu_buffer_rsrc_t r, void* dst, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+
+// LDS rows of CB 16-byte chunks keep chunk c of row r in slot c ^ lds_swz<CB>(r):
+// the chunk-c reads of 8 (or 16) consecutive rows then fall in 8 (16)
+// distinct 16-byte bank slots of a 128-byte (256-byte) window.
+template <int CB>
+__device__ __forceinline__ int lds_swz(int r) {
+  static_assert(CB == 1 || CB == 2 || CB == 4 || CB == 8 || CB == 16, "chunks per row");
+  if constexpr (CB == 1) return 0;
+  else if constexpr (CB == 2) return ((r >> 2) ^ (r >> 3)) & 1;
+  else if constexpr (CB == 4) return ((r >> 1) ^ (r >> 2)) & 3;
+  else if constexpr (CB == 8) return (r ^ (r >> 3)) & 7;
+  else return r & 15;
+}
+
 }  // namespace qlq

@@ -24,10 +24,11 @@
 // below 2^15 for every group of column n; e_m puts max|x[m,:]| in
 // [2^14, 2^15).
 //
-// Tiling: 256 threads (2x2 waves), block tile 128x128, k-iteration 64, wave
-// tile 64x64 = 2x2 MFMA 32x32x16 tiles, LDS double buffer fed from two
-// register stages (one barrier per k-iteration), XCD-aware tile order.  Codes
-// are dequantized once per block, while written to LDS.
+// Tiling: 512 threads, block tile 128x128, k-iteration 64; x16, packed codes
+// and the pre-scaled (s', b') pairs go straight from global memory into a
+// ring of LDS stages (one barrier per k-iteration); each wave dequantizes the
+// codes of its own B fragments after reading them from LDS, so codes cross
+// LDS at BITS/16 of the bytes of fp16 weights.  XCD-aware tile order.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile.hpp"
@@ -35,10 +36,10 @@
 namespace qlq {
 
 namespace gemm {
-constexpr int BM = 128, BN = 128, BK = 64, KS = 16;  // KS: MFMA k-step
-constexpr int THREADS = 256;
-constexpr int LDS_STRIDE = BK + 8;  // fp16 elements per LDS row (16-byte pad)
-constexpr int A_U4 = BM * BK / 8 / THREADS;  // 4 uint4 of x16 per thread per k-iteration
+constexpr int BM = 128, BN = 128;
+constexpr int WAVES = 4;     // waves per block (two blocks per compute unit)
+constexpr int KB = 64;       // k-iteration
+constexpr int NSTAGES = 2;   // LDS ring depth (double buffer: small enough for three blocks per CU)
 }  // namespace gemm
 
 __device__ __forceinline__ int floor_log2(float v) {  // v > 0, finite
@@ -48,10 +49,13 @@ __device__ __forceinline__ int floor_log2(float v) {  // v > 0, finite
 }
 
 // ------------------------------------------------------------------ pre-pass
-// Column exponents f_n: one thread per column n.
+// Column n: exponent f_n, then the fp16 pair (s', b') of every group, stored
+// group-major (sbt[g * NP + n], NP = N rounded up to 4) so that one k-range's
+// entries for a block of columns are contiguous.
 template <int BITS, typename XT>
 __device__ __forceinline__ void column_exponent(const XT* __restrict__ scales, const XT* __restrict__ biases,
-                                                int n, int ng, int* __restrict__ wexp) {
+                                                int n, int ng, int NP, int* __restrict__ wexp,
+                                                uint32_t* __restrict__ sbt) {
   constexpr float qmax = (float)((1 << BITS) - 1);
   int f = -1000;
   for (int g = 0; g < ng; ++g) {
@@ -61,7 +65,15 @@ __device__ __forceinline__ void column_exponent(const XT* __restrict__ scales, c
     if (s != 0.0f) f = max(f, floor_log2(fabsf(s)) + 10);
     if (top != 0.0f) f = max(f, floor_log2(top) - 14);
   }
-  wexp[n] = f == -1000 ? 0 : f;
+  f = f == -1000 ? 0 : f;
+  wexp[n] = f;
+  for (int g = 0; g < ng; ++g) {
+    const float s = Elem<XT>::load(scales, (int64_t)n * ng + g);
+    const float b = Elem<XT>::load(biases, (int64_t)n * ng + g);
+    const f16_t s16 = (f16_t)ldexpf(s, 24 - f), b16 = (f16_t)ldexpf(b, -f);
+    sbt[(int64_t)g * NP + n] = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, b16) << 16);
+  }
 }
 
 // x16[m, k] for one row held by one wave: element k of block b (PER codes)
@@ -73,14 +85,14 @@ template <int BITS, typename XT, int EPT>
 __global__ void __launch_bounds__(256)
 gemm_prep_wave_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ scales,
                       const XT* __restrict__ biases, int N, int G, f16_t* __restrict__ x16,
-                      int* __restrict__ xexp, int* __restrict__ wexp) {
+                      int* __restrict__ xexp, int* __restrict__ wexp, uint32_t* __restrict__ sbt) {
   constexpr int PER = 32 / BITS;
   constexpr int HALF = PER / 2;
   constexpr int G16 = EPT / 16;
   const int row_blocks = (M + 3) / 4;
   if ((int)blockIdx.x >= row_blocks) {
     const int n = ((int)blockIdx.x - row_blocks) * 256 + threadIdx.x;
-    if (n < N) column_exponent<BITS, XT>(scales, biases, n, K / G, wexp);
+    if (n < N) column_exponent<BITS, XT>(scales, biases, n, K / G, (N + 3) & ~3, wexp, sbt);
     return;
   }
   const int lane = threadIdx.x & 63;
@@ -127,13 +139,13 @@ template <int BITS, typename XT>
 __global__ void __launch_bounds__(256)
 gemm_prep_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ scales,
                  const XT* __restrict__ biases, int N, int G, f16_t* __restrict__ x16,
-                 int* __restrict__ xexp, int* __restrict__ wexp) {
+                 int* __restrict__ xexp, int* __restrict__ wexp, uint32_t* __restrict__ sbt) {
   constexpr int PER = 32 / BITS;  // codes per word = x block permuted together
   constexpr int HALF = PER / 2;
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= M) {
     const int n = ((int)blockIdx.x - M) * 256 + tid;
-    if (n < N) column_exponent<BITS, XT>(scales, biases, n, K / G, wexp);
+    if (n < N) column_exponent<BITS, XT>(scales, biases, n, K / G, (N + 3) & ~3, wexp, sbt);
     return;
   }
   __shared__ float red[4];
@@ -163,177 +175,266 @@ gemm_prep_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ 
 }
 
 // ------------------------------------------------------------------- GEMM
-template <int BITS, typename XT>
-__global__ void __launch_bounds__(gemm::THREADS, 1)
+// Block: WV waves, tile 128x128.  Wave (wq, kh) owns the 64x64 sub-tile wq
+// and, with 8 waves, half kh of every k-iteration's k-steps (the halves are
+// summed through LDS at the end); with 4 waves every wave takes all k-steps
+// and two blocks share a compute unit.  Per stage of the LDS ring:
+//   A  : 128 rows of x16, BK values (2*BK bytes) each, 16-byte chunks swizzled
+//   B  : 128 packed rows, RB = BK*BITS/8 bytes each, chunks swizzled
+//   SB : per 64-k sub-block, 512 bytes per group it touches: (s', b') of the
+//        block's 128 columns
+// all filled by buffer-to-LDS loads (out-of-range offsets write zeros).
+//
+// k order inside a 64-k sub-block.  The MFMA 32x32x16 f16 lane l holds 8
+// k-values of its row/column; half h = l / 32 and k-step s (0..3) pick which
+// 8.  Any order works if A and B agree, so the order is chosen to make each
+// lane's codes contiguous:
+//   4-bit: word 4h + s        (8 codes, pairs (j, j+4))        A chunk 4h + s
+//   8-bit: words 8h+2s, +1    (2 x 4 codes, pairs (0,2),(1,3)) A chunk 4h + s
+//   2-bit: word s, pairs 4h..4h+3 of (j, j+8)                 A chunk 2s + h
+// (x16 already holds every word's values in the pair order).
+namespace gemm {
+template <int BITS, int BK, int STAGES, int WV> struct Cfg {
+  static constexpr int KSPLIT = WV / 4;             // waves per sub-tile (k-split)
+  static constexpr int SPW = 4 / KSPLIT;            // k-steps per wave per 64-k sub-block
+  static constexpr int U = BK / 64;                 // 64-k sub-blocks per k-iteration
+  static constexpr int A_ROW = 2 * BK;              // bytes per A row
+  static constexpr int A_CB = A_ROW / 16;           // chunks per A row
+  static constexpr int A_TILE = BM * A_ROW;
+  static constexpr int RB = BK * BITS / 8;          // bytes per packed row per k-iteration
+  static constexpr int B_CB = RB / 16;              // chunks per packed row
+  static constexpr int B_TILE = BN * RB;
+  static constexpr int SB_OFF = A_TILE + B_TILE;
+  static constexpr int STAGE = SB_OFF + U * 1024;
+  static constexpr int A_RPI = 1024 / A_ROW;        // A rows per wave-wide load
+  static constexpr int B_RPI = 1024 / RB;           // B rows per wave-wide load
+  static constexpr int A_LOADS = A_TILE / 1024;     // wave-wide loads per stage
+  static constexpr int B_LOADS = B_TILE / 1024;
+  static constexpr int APW = A_LOADS / WV;          // A loads per wave
+  static constexpr int NO = B_LOADS + U;            // B and SB loads, dealt round-robin
+  static constexpr int LW = APW + NO / WV;          // loads per wave per stage (waves < NO % WV: +1)
+  static constexpr int LDS = STAGES * STAGE > 4 * 64 * 64 * 4 || KSPLIT == 1 ? STAGES * STAGE : 4 * 64 * 64 * 4;
+  static_assert(WV == 4 || WV == 8, "waves");
+  static_assert(A_LOADS % WV == 0 && B_TILE % 1024 == 0, "tile split");
+  static_assert((STAGES - 2) * (LW + 1) < 64, "vmcnt field");
+  static_assert(LDS * (KSPLIT == 1 ? 2 : 1) <= 160 * 1024, "LDS");
+};
+}  // namespace gemm
+
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int BITS, typename XT, int BK, int STAGES, int WV>
+__global__ void __launch_bounds__(64 * WV, 8 / WV)
 affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, int M, int K,
-                   const uint32_t* __restrict__ packed, const XT* __restrict__ scales,
-                   const XT* __restrict__ biases, const int* __restrict__ wexp, int N, int G,
-                   const XT* __restrict__ bias, XT* __restrict__ y) {
+                   const uint32_t* __restrict__ packed, const uint32_t* __restrict__ sbt,
+                   const int* __restrict__ wexp, int N, int G, const XT* __restrict__ bias,
+                   XT* __restrict__ y) {
   using namespace gemm;
-  constexpr int PER = 32 / BITS;                     // codes per word
-  constexpr int WROW = BK / PER;                     // words per B row per k-iteration
-  constexpr int B_U4 = BN * WROW / 4;                // uint4 of codes per k-iteration
-  constexpr int B_U4_T = (B_U4 + THREADS - 1) / THREADS;
-  constexpr int U4_PER_ROW = WROW / 4;               // 1 (2-bit), 2 (4-bit), 4 (8-bit)
+  using C = Cfg<BITS, BK, STAGES, WV>;
+  constexpr int PER = 32 / BITS;
+  constexpr int SPW = C::SPW;
   constexpr uint32_t MASK = ((1u << BITS) - 1u) * 0x00010001u;
+  __shared__ __attribute__((aligned(16))) int8_t smem[C::LDS];
 
-  __shared__ __attribute__((aligned(16))) f16_t As[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) f16_t Bs[2][BN * LDS_STRIDE];
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches below
+  const int wq = wid & 3, kh = wid >> 2, wm = wq >> 1, wn = wq & 1, h = lane >> 5;
   int tm, tn;
   tile_coords<8>(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   const int m_blk = tm * BM, n_blk = tn * BN;
-  const int nk = K / BK;        // K % BK == 0 on this path
-  const int ng = K / G;
-  const int wpr = K / PER;      // words per packed row
+  const int nk = (K + BK - 1) / BK;  // K % 64 == 0; a last half-iteration reads zeros
+  const int rowb = K / PER * 4;      // bytes per packed row
+  const int ng = K / G, NP = (N + 3) & ~3;
+  const int lg_g = 31 - __builtin_clz(G);  // G is a power of two
 
-  // A: rows of x16
-  const f16_t* ap[A_U4];
-  int a_lofs[A_U4];
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x16 + (int64_t)m_blk * K, min(BM, M - m_blk) * K * 2);
+  const __amdgpu_buffer_rsrc_t rsb =
+      make_rsrc(reinterpret_cast<const int8_t*>(packed) + (int64_t)n_blk * rowb, min(BN, N - n_blk) * rowb);
+  const __amdgpu_buffer_rsrc_t rss = make_rsrc(sbt, ng * NP * 4);
+
+  // ---- loads of one stage: this wave's A loads, then its share of the B
+  // and SB loads (other-load o goes to wave o % WV)
+  int a_off[C::APW], a_k[C::APW];
 #pragma unroll
-  for (int i = 0; i < A_U4; ++i) {
-    const int idx = tid + THREADS * i, r = idx / (BK / 8), c = idx % (BK / 8);
-    ap[i] = x16 + (int64_t)min(m_blk + r, M - 1) * K + c * 8;
-    a_lofs[i] = r * LDS_STRIDE + c * 8;
+  for (int j = 0; j < C::APW; ++j) {
+    const int r = (wid * C::APW + j) * C::A_RPI + lane / C::A_CB;
+    const int c = (lane % C::A_CB) ^ lds_swz<C::A_CB>(r);
+    a_off[j] = r * K * 2 + c * 16;
+    a_k[j] = c * 8;  // first k of the chunk within the k-iteration
   }
-  // B: this thread's packed-code uint4 (fixed row, fixed k offset in the tile)
-  const uint32_t* bp[B_U4_T];
-  int b_lofs[B_U4_T], b_kofs[B_U4_T];
-  int64_t b_gbase[B_U4_T];
-  int b_fexp[B_U4_T];  // f_n of this thread's row
-  bool b_on[B_U4_T];
-  // 2-bit codes: one uint4 holds 64 codes, which may span two groups of 32
-  constexpr int SBN = BITS == 2 ? 2 : 1;
+  constexpr int OMAX = (C::NO + WV - 1) / WV;
+  int o_off[OMAX], o_k[OMAX];  // B: byte offset and first k; SB: entry offset and first k
 #pragma unroll
-  for (int i = 0; i < B_U4_T; ++i) {
-    const int idx = tid + THREADS * i;
-    b_on[i] = idx < B_U4;
-    const int r = b_on[i] ? idx / U4_PER_ROW : 0, c = idx % U4_PER_ROW;
-    const int n = min(n_blk + r, N - 1);
-    bp[i] = packed + (int64_t)n * wpr + c * 4;
-    b_lofs[i] = r * LDS_STRIDE + c * 4 * PER;
-    b_kofs[i] = c * 4 * PER;
-    b_gbase[i] = (int64_t)n * ng;
-    b_fexp[i] = wexp[n];
+  for (int t = 0; t < OMAX; ++t) {
+    const int o = wid + WV * t;
+    o_off[t] = 0;
+    o_k[t] = 0;
+    if (o < C::B_LOADS) {
+      const int r = o * C::B_RPI + lane / C::B_CB;
+      const int c = (lane % C::B_CB) ^ lds_swz<C::B_CB>(r);
+      o_off[t] = r * rowb + c * 16;
+      o_k[t] = c * 16 * 8 / BITS;
+    } else if (o < C::NO) {
+      // sub-block u = o - B_LOADS: lanes 0-31 its first group, lanes 32-63
+      // the second one when a sub-block spans two groups (else the first again)
+      const int u = o - C::B_LOADS;
+      o_off[t] = n_blk * 4 + (lane & 31) * 16;
+      o_k[t] = u * 64 + (G < 64 ? (lane >> 5) * G : 0);
+    }
   }
+  const int n_other = C::NO / WV + (wid < C::NO % WV ? 1 : 0);
 
-  u32x4_v ra0[A_U4], ra1[A_U4], rb0[B_U4_T], rb1[B_U4_T];
-  uint32_t rs0[B_U4_T][SBN], rs1[B_U4_T][SBN], rbi0[B_U4_T][SBN], rbi1[B_U4_T][SBN];  // raw 16-bit scale, bias
-
-  // Stage operations, written as macros so that every register-array index is
-  // a literal and the arrays stay in registers.  The load stage only issues
-  // loads: any use of a loaded register there would make the compiler wait
-  // for it at once and serialise the prefetch.
-#define QLQ_LOAD(ST, IT)                                                                 \
-  do {                                                                                   \
-    const int k0_ = (IT) * BK;                                                           \
-    _Pragma("unroll") for (int i = 0; i < A_U4; ++i)                                     \
-        ra##ST[i] = *reinterpret_cast<const u32x4_v*>(ap[i] + k0_);                        \
-    _Pragma("unroll") for (int i = 0; i < B_U4_T; ++i) {                                 \
-      if (B_U4 % THREADS == 0 || b_on[i]) {                                              \
-        rb##ST[i] = *reinterpret_cast<const u32x4_v*>(bp[i] + k0_ / PER);                  \
-        _Pragma("unroll") for (int h = 0; h < SBN; ++h) {                                \
-          const int64_t g_ = b_gbase[i] + (k0_ + b_kofs[i] + 32 * h) / G;               \
-          rs##ST[i][h] = reinterpret_cast<const uint16_t*>(scales)[g_];                  \
-          rbi##ST[i][h] = reinterpret_cast<const uint16_t*>(biases)[g_];                 \
-        }                                                                                \
-      }                                                                                  \
-    }                                                                                    \
+#define QLQ_ISSUE(T)                                                                              \
+  do {                                                                                            \
+    const int k0_ = (T) * BK;                                                                     \
+    int8_t* st_ = smem + ((T) % STAGES) * C::STAGE;                                               \
+    _Pragma("unroll") for (int j = 0; j < C::APW; ++j) {                                          \
+      const int kk_ = k0_ + a_k[j];                                                               \
+      load_lds_b128(rsa, st_ + (wid * C::APW + j) * 1024, kk_ < K ? a_off[j] + k0_ * 2 : kOutOfRange); \
+    }                                                                                             \
+    _Pragma("unroll") for (int t = 0; t < OMAX; ++t) {                                            \
+      const int o_ = wid + WV * t;                                                                \
+      if (t < n_other) {                                                                          \
+        const int kk_ = k0_ + o_k[t];                                                             \
+        if (o_ < C::B_LOADS)                                                                      \
+          load_lds_b128(rsb, st_ + C::A_TILE + o_ * 1024,                                         \
+                        kk_ < K ? o_off[t] + k0_ / PER * 4 : kOutOfRange);                        \
+        else                                                                                      \
+          load_lds_b128(rss, st_ + C::SB_OFF + (o_ - C::B_LOADS) * 1024,                         \
+                        kk_ < K ? o_off[t] + (kk_ >> lg_g) * NP * 4 : kOutOfRange);               \
+      }                                                                                           \
+    }                                                                                             \
   } while (0)
 
-#define QLQ_STORE(ST, BUF)                                                               \
-  do {                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < A_U4; ++i)                                     \
-        *reinterpret_cast<u32x4_v*>(&As[BUF][a_lofs[i]]) = ra##ST[i];                      \
-    _Pragma("unroll") for (int i = 0; i < B_U4_T; ++i) {                                 \
-      if (B_U4 % THREADS == 0 || b_on[i]) {                                              \
-        f16x2_v s2_[SBN], b2_[SBN];                                                      \
-        _Pragma("unroll") for (int h = 0; h < SBN; ++h) {                                \
-          const float s_ = bits16_to_f32<XT>((uint16_t)rs##ST[i][h]);                    \
-          const float bb_ = bits16_to_f32<XT>((uint16_t)rbi##ST[i][h]);                  \
-          const f16_t s16_ = (f16_t)ldexpf(s_, 24 - b_fexp[i]);                          \
-          const f16_t b16_ = (f16_t)ldexpf(bb_, -b_fexp[i]);                             \
-          s2_[h] = f16x2_v{s16_, s16_};                                                  \
-          b2_[h] = f16x2_v{b16_, b16_};                                                  \
-        }                                                                                \
-        const uint32_t w4_[4] = {rb##ST[i][0], rb##ST[i][1], rb##ST[i][2], rb##ST[i][3]};    \
-        uint32_t d_[2 * PER];                                                            \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                  \
-          const int h_ = SBN == 2 ? t / 2 : 0;                                           \
-          _Pragma("unroll") for (int j = 0; j < PER / 2; ++j) {                          \
-            const uint32_t qd_ = (w4_[t] >> (BITS * j)) & MASK;                          \
-            const f16x2_v wv_ =                                                          \
-                __builtin_elementwise_fma(s2_[h_], __builtin_bit_cast(f16x2_v, qd_), b2_[h_]); \
-            d_[t * (PER / 2) + j] = __builtin_bit_cast(uint32_t, wv_);                   \
-          }                                                                              \
-        }                                                                                \
-        f16_t* dst_ = &Bs[BUF][b_lofs[i]];                                               \
-        _Pragma("unroll") for (int q = 0; q < PER / 2; ++q)                              \
-            *reinterpret_cast<u32x4_v*>(dst_ + 8 * q) =                                  \
-                u32x4_v{d_[4 * q], d_[4 * q + 1], d_[4 * q + 2], d_[4 * q + 3]};         \
-      }                                                                                  \
-    }                                                                                    \
-  } while (0)
+  // ---- fragment addresses inside a stage.  This wave's k-steps of a
+  // sub-block are s = kh*SPW + sl, sl < SPW.
+  // B: the words of those steps are contiguous: NBW words from byte boff
+  constexpr int NBW = BITS == 8 ? 2 * SPW : SPW;
+  // SB: 2-bit codes with 32-wide groups change group between steps 1 and 2
+  constexpr bool SB2 = BITS == 2 && SPW == 4;
+  constexpr int NBR = NBW == 8 ? 2 : 1;  // 16-byte B reads per fragment
+  int aoff[2][C::U][SPW];
+  int boff[2][C::U][NBR];
+  int soff[2][C::U];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ra = wm * 64 + 32 * i + (lane & 31), rb = wn * 64 + 32 * i + (lane & 31);
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+#pragma unroll
+      for (int sl = 0; sl < SPW; ++sl) {
+        const int st = kh * SPW + sl;
+        const int c = 8 * u + (BITS == 2 ? 2 * st + h : 4 * h + st);
+        aoff[i][u][sl] = ra * C::A_ROW + (c ^ lds_swz<C::A_CB>(ra)) * 16;
+      }
+      // first word of this wave's steps within the row's sub-block
+      const int w0 = BITS == 4 ? 4 * h + kh * SPW : BITS == 2 ? kh * SPW : 8 * h + 2 * kh * SPW;
+      const int cb = (C::RB / C::U / 16) * u + w0 / 4;  // chunk (4 words per chunk)
+#pragma unroll
+      for (int q = 0; q < NBR; ++q)
+        boff[i][u][q] = C::A_TILE + rb * C::RB + ((cb + q) ^ lds_swz<C::B_CB>(rb)) * 16 + (w0 % 4) * 4;
+      const int gi = G < 64 ? (BITS == 2 ? kh : h) : 0;
+      soff[i][u] = C::SB_OFF + u * 1024 + gi * 512 + rb * 4;
+    }
+  }
 
-  // 32x32x16 fp16 MFMA: lane l holds 8 consecutive k of row (A) / column (B)
-  // l % 32 at k offset 8 * (l / 32); result element e of lane l is row
-  // 8*(e/4) + 4*(l/32) + e%4, column l % 32.
   f32x16_v acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_v{};
 
-  const int a_row = wm * 64 + (lane & 31), b_row = wn * 64 + (lane & 31);
-  const int kofs = (lane >> 5) * 8;
-#define QLQ_COMPUTE(BUF)                                                                             \
-  do {                                                                                               \
-    _Pragma("unroll") for (int ks = 0; ks < BK; ks += KS) {                                          \
-      u32x4_v af_[2], bf_[2];                                                                        \
-      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                                  \
-          af_[i] = *reinterpret_cast<const u32x4_v*>(&As[BUF][(a_row + 32 * i) * LDS_STRIDE + ks + kofs]); \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                  \
-          bf_[j] = *reinterpret_cast<const u32x4_v*>(&Bs[BUF][(b_row + 32 * j) * LDS_STRIDE + ks + kofs]); \
-      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                                  \
-          _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =                                  \
-              __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_v, af_[i]),            \
-                                                     __builtin_bit_cast(f16x8_v, bf_[j]), acc[i][j], 0, 0, 0); \
-    }                                                                                                \
-  } while (0)
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t) QLQ_ISSUE(t);
+  for (int it = 0; it < nk; ++it) {
+    // this wave's loads of tile it have landed once at most the later
+    // STAGES-2 tiles' loads are outstanding; then the barrier
+    if (n_other == C::NO / WV) wait_loads_and_barrier<(STAGES - 2) * C::LW>();
+    else wait_loads_and_barrier<(STAGES - 2) * (C::LW + 1)>();
+    QLQ_ISSUE(it + STAGES - 1);
+    const int8_t* st = smem + (it % STAGES) * C::STAGE;
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      u32x4_v af[2][SPW];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) af[i][sl] = *reinterpret_cast<const u32x4_v*>(st + aoff[i][u][sl]);
+      u32x4_v bq[2][SPW];  // [j][sl]: dequantized B operands
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint32_t e[2];
+        e[0] = *reinterpret_cast<const uint32_t*>(st + soff[j][u]);
+        e[1] = e[0];
+        if constexpr (SB2)
+          if (G < 64) e[1] = *reinterpret_cast<const uint32_t*>(st + soff[j][u] + 512);
+        uint32_t w[NBW];
+        if constexpr (NBW == 2) {
+          const uint2 v = *reinterpret_cast<const uint2*>(st + boff[j][u][0]);
+          w[0] = v.x; w[1] = v.y;
+        } else {
+#pragma unroll
+          for (int q = 0; q < NBR; ++q) {
+            const u32x4_v v = *reinterpret_cast<const u32x4_v*>(st + boff[j][u][q]);
+            w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
+          }
+        }
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) {
+          const uint32_t ee = SB2 && sl >= 2 ? e[1] : e[0];
+          const f16x2_v s2 = __builtin_bit_cast(f16x2_v, (ee & 0xFFFFu) * 0x10001u);
+          const f16x2_v b2 = __builtin_bit_cast(f16x2_v, (ee >> 16) * 0x10001u);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            uint32_t qd;
+            if constexpr (BITS == 4) qd = (w[sl] >> (4 * p)) & MASK;
+            else if constexpr (BITS == 2) qd = (w[sl] >> (2 * (4 * h + p))) & MASK;
+            else qd = (w[2 * sl + (p >> 1)] >> (8 * (p & 1))) & MASK;
+            bq[j][sl][p] = __builtin_bit_cast(uint32_t,
+                                              __builtin_elementwise_fma(s2, __builtin_bit_cast(f16x2_v, qd), b2));
+          }
+        }
+      }
+#pragma unroll
+      for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_v, af[i][sl]),
+                                                              __builtin_bit_cast(f16x8_v, bq[j][sl]),
+                                                              acc[i][j], 0, 0, 0);
+    }
+  }
+#undef QLQ_ISSUE
+  // the zero tiles issued past the end may still be landing in the ring
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // Loads past the last tile re-read the last tile (clamped index) and the
-  // matching stores fill the idle buffer: both are harmless and keep the loop
-  // body free of conditional register writes.
-  const int last = nk - 1;
-  QLQ_LOAD(0, 0);
-  QLQ_LOAD(1, min(1, last));
-  QLQ_STORE(0, 0);
-  QLQ_LOAD(0, min(2, last));
-  // The loop body holds a whole even/odd pair with no exit in between: an
-  // exit there lets the compiler sink one stage's loads down to their first
-  // use, which removes the prefetch.  An odd last tile is finished after it.
-  int it = 0;
-  for (; it + 1 < nk; it += 2) {
-    // even step: compute buffer 0; stage 1 (tile it+1) -> buffer 1
+  if constexpr (C::KSPLIT == 2) {
+    // ---- join the two k-halves: waves 4-7 park their sums in LDS, waves
+    // 0-3 add them and run the epilogue
+    float* red = reinterpret_cast<float*>(smem);  // 4 sub-tiles x 64 values x 64 lanes
     __syncthreads();
-    QLQ_STORE(1, 1);
-    QLQ_LOAD(1, min(it + 3, last));
-    QLQ_COMPUTE(0);
-    // odd step: compute buffer 1; stage 0 (tile it+2) -> buffer 0
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) red[(wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane] = acc[i][j][e];
+    }
     __syncthreads();
-    QLQ_STORE(0, 0);
-    QLQ_LOAD(0, min(it + 4, last));
-    QLQ_COMPUTE(1);
+    if (kh == 1) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] += red[(wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane];
   }
-  if (it < nk) {  // odd nk: buffer 0 holds the last tile
-    __syncthreads();
-    QLQ_COMPUTE(0);
-  }
-#undef QLQ_LOAD
-#undef QLQ_STORE
-#undef QLQ_COMPUTE
 
   // ---- epilogue: y = 2^(e_m + f_n) * acc + bias, one rounding
   int fcol[2];
@@ -363,40 +464,51 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
   }
 }
 
-size_t affine_gemm_workspace(int64_t M, int64_t K, int64_t N) {
-  size_t x16 = ((size_t)M * (size_t)K * 2 + 255) & ~(size_t)255;
-  size_t xe = ((size_t)M * 4 + 255) & ~(size_t)255;
-  return x16 + xe + (size_t)N * 4;
-}
+// Workspace: x16 [M, K] fp16 | e_m [M] | f_n [N] | (s', b') [K/G, NP], each
+// part 256-byte aligned.
+struct GemmWs {
+  size_t x16, xe, we, sb, total;
+  GemmWs(int64_t M, int64_t K, int64_t N, int G) {
+    const auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    x16 = 0;
+    xe = al((size_t)M * (size_t)K * 2);
+    we = xe + al((size_t)M * 4);
+    sb = we + al((size_t)N * 4);
+    total = sb + (size_t)(K / G) * (size_t)((N + 3) & ~3) * 4;
+  }
+};
+
+size_t affine_gemm_workspace(int64_t M, int64_t K, int64_t N, int G) { return GemmWs(M, K, N, G).total; }
 
 template <int BITS, typename XT>
 static hipError_t gemm_launch(const void* x, int64_t M, int64_t K, const uint32_t* packed,
                               const void* scales, const void* biases, int64_t N, int G,
                               const void* bias, void* y, void* ws, hipStream_t s) {
-  f16_t* x16 = (f16_t*)ws;
-  const size_t x16b = ((size_t)M * (size_t)K * 2 + 255) & ~(size_t)255;
-  int* xexp = (int*)((char*)ws + x16b);
-  int* wexp = (int*)((char*)ws + x16b + (((size_t)M * 4 + 255) & ~(size_t)255));
+  const GemmWs L(M, K, N, G);
+  f16_t* x16 = (f16_t*)((char*)ws + L.x16);
+  int* xexp = (int*)((char*)ws + L.xe);
+  int* wexp = (int*)((char*)ws + L.we);
+  uint32_t* sbt = (uint32_t*)((char*)ws + L.sb);
   const int m = (int)M, n = (int)N, k = (int)K;
   if (K <= 64 * 64) {
     const unsigned blocks = (unsigned)(cdiv(M, 4) + cdiv(N, 256));
 #define QLQ_PREP(EPT_)                                                                                  \
   hipLaunchKernelGGL((gemm_prep_wave_kernel<BITS, XT, EPT_>), dim3(blocks), dim3(256), 0, s, (const XT*)x, m, \
-                     k, (const XT*)scales, (const XT*)biases, n, G, x16, xexp, wexp)
+                     k, (const XT*)scales, (const XT*)biases, n, G, x16, xexp, wexp, sbt)
     if (K <= 64 * 16) QLQ_PREP(16);
     else if (K <= 64 * 32) QLQ_PREP(32);
     else QLQ_PREP(64);
 #undef QLQ_PREP
   } else {
     hipLaunchKernelGGL((gemm_prep_kernel<BITS, XT>), dim3((unsigned)(M + cdiv(N, 256))), dim3(256), 0, s,
-                       (const XT*)x, m, k, (const XT*)scales, (const XT*)biases, n, G, x16, xexp, wexp);
+                       (const XT*)x, m, k, (const XT*)scales, (const XT*)biases, n, G, x16, xexp, wexp, sbt);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tiles = cdiv(M, gemm::BM) * cdiv(N, gemm::BN);
-  hipLaunchKernelGGL((affine_gemm_kernel<BITS, XT>), dim3((unsigned)tiles), dim3(gemm::THREADS), 0, s,
-                     (const f16_t*)x16, (const int*)xexp, m, k, packed, (const XT*)scales, (const XT*)biases,
-                     (const int*)wexp, n, G, (const XT*)bias, (XT*)y);
+  hipLaunchKernelGGL((affine_gemm_kernel<BITS, XT, gemm::KB, gemm::NSTAGES, gemm::WAVES>), dim3((unsigned)tiles),
+                     dim3(64 * gemm::WAVES), 0, s, (const f16_t*)x16, (const int*)xexp, m, k, packed,
+                     (const uint32_t*)sbt, (const int*)wexp, n, G, (const XT*)bias, (XT*)y);
   return hipGetLastError();
 }
 

@@ -44,9 +44,7 @@ template <int BK, int STAGES> struct Cfg {
   static constexpr int VMCNT = (STAGES - 2) * LPT;  // loads allowed outstanding at the wait
   static_assert(BM == BN && (BK == 128 || BK == 256) && ROWS_W % RPI == 0, "tile shape");
   static_assert(STAGES >= 2 && VMCNT < 64, "ring depth");
-  // slot of chunk c in row r is c ^ swz(r): 8 or 16 consecutive rows read at
-  // one chunk land on distinct banks
-  static __device__ __forceinline__ int swz(int r) { return BK == 128 ? ((r + (r >> 3)) & 7) : (r & 15); }
+  static __device__ __forceinline__ int swz(int r) { return lds_swz<CPR>(r); }
 };
 }  // namespace i8
 
@@ -58,8 +56,6 @@ __device__ __forceinline__ i32x16_v mma_i8(u32x4_v a, u32x4_v b, i32x16_v c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_v, a), __builtin_bit_cast(i32x4_v, b),
                                                 c, 0, 0, 0);
 }
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Pipeline (one barrier per k-iteration).  Before iteration `it`, tiles
 // it .. it+STAGES-2 are in flight to their ring slots.  Iteration it: wait
@@ -105,8 +101,8 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
     int8_t* dst_ = smem + ((T) % STAGES) * C::STAGE + wid * ROWS_W * BK;                        \
     _Pragma("unroll") for (int j = 0; j < C::LPW; ++j) {                                        \
       const int o_ = k0_ + kc[j] < K ? voff[j] + k0_ : kOutOfRange;                             \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(dst_ + 1024 * j), 16, o_, 0, 0, 0);           \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(dst_ + C::TILE + 1024 * j), 16, o_, 0, 0, 0); \
+      load_lds_b128(rsa, dst_ + 1024 * j, o_);                                                  \
+      load_lds_b128(rsb, dst_ + C::TILE + 1024 * j, o_);                                        \
     }                                                                                           \
   } while (0)
 

@@ -29,7 +29,7 @@ hipError_t launch_affine_gemv(const void* x, int x_dtype, int64_t M, int64_t K,
                               hipStream_t s);
 
 // gemm.hip: affine prefill GEMM (bf16 / f16 x)
-size_t affine_gemm_workspace(int64_t M, int64_t K, int64_t N);
+size_t affine_gemm_workspace(int64_t M, int64_t K, int64_t N, int group_size);
 hipError_t launch_affine_gemm(const void* x, int x_dtype, int64_t M, int64_t K,
                               const uint32_t* packed, const void* scales, const void* biases,
                               int64_t N, int bits, int G, const void* bias, void* y,
