@@ -24,7 +24,8 @@
 // below 2^15 for every group of column n; e_m puts max|x[m,:]| in
 // [2^14, 2^15).
 //
-// Tiling: 512 threads, block tile 128x128, k-iteration 64; x16, packed codes
+// Tiling: 256 threads, block tile 256x128 (128x128 for few tiles), k-iteration
+// 64; x16, packed codes
 // and the pre-scaled (s', b') pairs go straight from global memory into a
 // ring of LDS stages (one barrier per k-iteration); each wave dequantizes the
 // codes of its own B fragments after reading them from LDS, so codes cross
@@ -36,10 +37,13 @@
 namespace qlq {
 
 namespace gemm {
-constexpr int BM = 128, BN = 128;
+constexpr int BN = 128;  // block columns
 constexpr int WAVES = 4;     // waves per block (two blocks per compute unit)
 constexpr int KB = 64;       // k-iteration
 constexpr int NSTAGES = 2;   // LDS ring depth (double buffer: small enough for three blocks per CU)
+// block rows: 256 (wave tile 128x64, half the dequantization per MFMA of
+// 128-row blocks) when that still gives two blocks per compute unit
+constexpr int TILE_M_TALL = 256, TILE_M = 128;
 }  // namespace gemm
 
 __device__ __forceinline__ int floor_log2(float v) {  // v > 0, finite
@@ -194,13 +198,14 @@ gemm_prep_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ 
 //   2-bit: word s, pairs 4h..4h+3 of (j, j+8)                 A chunk 2s + h
 // (x16 already holds every word's values in the pair order).
 namespace gemm {
-template <int BITS, int BK, int STAGES, int WV> struct Cfg {
+template <int BITS, int BK, int STAGES, int WV, int BMT> struct Cfg {
   static constexpr int KSPLIT = WV / 4;             // waves per sub-tile (k-split)
+  static constexpr int MI = BMT / 64;               // MFMA row tiles per wave (wave tile BMT/2 x 64)
   static constexpr int SPW = 4 / KSPLIT;            // k-steps per wave per 64-k sub-block
   static constexpr int U = BK / 64;                 // 64-k sub-blocks per k-iteration
   static constexpr int A_ROW = 2 * BK;              // bytes per A row
   static constexpr int A_CB = A_ROW / 16;           // chunks per A row
-  static constexpr int A_TILE = BM * A_ROW;
+  static constexpr int A_TILE = BMT * A_ROW;
   static constexpr int RB = BK * BITS / 8;          // bytes per packed row per k-iteration
   static constexpr int B_CB = RB / 16;              // chunks per packed row
   static constexpr int B_TILE = BN * RB;
@@ -215,6 +220,7 @@ template <int BITS, int BK, int STAGES, int WV> struct Cfg {
   static constexpr int LW = APW + NO / WV;          // loads per wave per stage (waves < NO % WV: +1)
   static constexpr int LDS = STAGES * STAGE > 4 * 64 * 64 * 4 || KSPLIT == 1 ? STAGES * STAGE : 4 * 64 * 64 * 4;
   static_assert(WV == 4 || WV == 8, "waves");
+  static_assert(BMT % 64 == 0 && BMT <= 256 && (KSPLIT == 1 || BMT == 128), "block rows");
   static_assert(A_LOADS % WV == 0 && B_TILE % 1024 == 0, "tile split");
   static_assert((STAGES - 2) * (LW + 1) < 64, "vmcnt field");
   static_assert(LDS * (KSPLIT == 1 ? 2 : 1) <= 160 * 1024, "LDS");
@@ -226,14 +232,15 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int BITS, typename XT, int BK, int STAGES, int WV>
+template <int BITS, typename XT, int BK, int STAGES, int WV, int BMT>
 __global__ void __launch_bounds__(64 * WV, 8 / WV)
 affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, int M, int K,
                    const uint32_t* __restrict__ packed, const uint32_t* __restrict__ sbt,
                    const int* __restrict__ wexp, int N, int G, const XT* __restrict__ bias,
                    XT* __restrict__ y) {
   using namespace gemm;
-  using C = Cfg<BITS, BK, STAGES, WV>;
+  using C = Cfg<BITS, BK, STAGES, WV, BMT>;
+  constexpr int MI = C::MI;
   constexpr int PER = 32 / BITS;
   constexpr int SPW = C::SPW;
   constexpr uint32_t MASK = ((1u << BITS) - 1u) * 0x00010001u;
@@ -243,14 +250,14 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches below
   const int wq = wid & 3, kh = wid >> 2, wm = wq >> 1, wn = wq & 1, h = lane >> 5;
   int tm, tn;
-  tile_coords<8>(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  const int m_blk = tm * BM, n_blk = tn * BN;
+  tile_coords<8>(blockIdx.x, (M + BMT - 1) / BMT, (N + BN - 1) / BN, tm, tn);
+  const int m_blk = tm * BMT, n_blk = tn * BN;
   const int nk = (K + BK - 1) / BK;  // K % 64 == 0; a last half-iteration reads zeros
   const int rowb = K / PER * 4;      // bytes per packed row
   const int ng = K / G, NP = (N + 3) & ~3;
   const int lg_g = 31 - __builtin_clz(G);  // G is a power of two
 
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x16 + (int64_t)m_blk * K, min(BM, M - m_blk) * K * 2);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(x16 + (int64_t)m_blk * K, min(BMT, M - m_blk) * K * 2);
   const __amdgpu_buffer_rsrc_t rsb =
       make_rsrc(reinterpret_cast<const int8_t*>(packed) + (int64_t)n_blk * rowb, min(BN, N - n_blk) * rowb);
   const __amdgpu_buffer_rsrc_t rss = make_rsrc(sbt, ng * NP * 4);
@@ -316,20 +323,26 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
   // SB: 2-bit codes with 32-wide groups change group between steps 1 and 2
   constexpr bool SB2 = BITS == 2 && SPW == 4;
   constexpr int NBR = NBW == 8 ? 2 : 1;  // 16-byte B reads per fragment
-  int aoff[2][C::U][SPW];
+  int aoff[MI][C::U][SPW];
   int boff[2][C::U][NBR];
   int soff[2][C::U];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int ra = wm * 64 + 32 * i + (lane & 31), rb = wn * 64 + 32 * i + (lane & 31);
+  for (int i = 0; i < MI; ++i) {
+    const int ra = wm * (BMT / 2) + 32 * i + (lane & 31);
 #pragma unroll
-    for (int u = 0; u < C::U; ++u) {
+    for (int u = 0; u < C::U; ++u)
 #pragma unroll
       for (int sl = 0; sl < SPW; ++sl) {
         const int st = kh * SPW + sl;
         const int c = 8 * u + (BITS == 2 ? 2 * st + h : 4 * h + st);
         aoff[i][u][sl] = ra * C::A_ROW + (c ^ lds_swz<C::A_CB>(ra)) * 16;
       }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rb = wn * 64 + 32 * i + (lane & 31);
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
       // first word of this wave's steps within the row's sub-block
       const int w0 = BITS == 4 ? 4 * h + kh * SPW : BITS == 2 ? kh * SPW : 8 * h + 2 * kh * SPW;
       const int cb = (C::RB / C::U / 16) * u + w0 / 4;  // chunk (4 words per chunk)
@@ -341,9 +354,9 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
     }
   }
 
-  f32x16_v acc[2][2];
+  f32x16_v acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_v{};
 
@@ -358,9 +371,9 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
     const int8_t* st = smem + (it % STAGES) * C::STAGE;
 #pragma unroll
     for (int u = 0; u < C::U; ++u) {
-      u32x4_v af[2][SPW];
+      u32x4_v af[MI][SPW];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int sl = 0; sl < SPW; ++sl) af[i][sl] = *reinterpret_cast<const u32x4_v*>(st + aoff[i][u][sl]);
       u32x4_v bq[2][SPW];  // [j][sl]: dequantized B operands
@@ -401,7 +414,7 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
 #pragma unroll
       for (int sl = 0; sl < SPW; ++sl)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_v, af[i][sl]),
@@ -446,10 +459,10 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
     bcol[j] = bias ? Elem<XT>::load(bias, n) : 0.0f;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int m = m_blk + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const int m = m_blk + wm * (BMT / 2) + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
       if (m >= M) continue;
       const int em = xexp[m];
 #pragma unroll
@@ -505,10 +518,16 @@ static hipError_t gemm_launch(const void* x, int64_t M, int64_t K, const uint32_
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t tiles = cdiv(M, gemm::BM) * cdiv(N, gemm::BN);
-  hipLaunchKernelGGL((affine_gemm_kernel<BITS, XT, gemm::KB, gemm::NSTAGES, gemm::WAVES>), dim3((unsigned)tiles),
-                     dim3(64 * gemm::WAVES), 0, s, (const f16_t*)x16, (const int*)xexp, m, k, packed,
-                     (const uint32_t*)sbt, (const int*)wexp, n, G, (const XT*)bias, (XT*)y);
+  // (8-bit codes: a 256-row stage does not fit twice in a compute unit's LDS)
+  const int64_t tall_tiles = cdiv(M, gemm::TILE_M_TALL) * cdiv(N, gemm::BN);
+  const bool tall = BITS != 8 && tall_tiles >= 2 * 256;
+  const int64_t tiles = tall ? tall_tiles : cdiv(M, gemm::TILE_M) * cdiv(N, gemm::BN);
+  auto kern = affine_gemm_kernel<BITS, XT, gemm::KB, gemm::NSTAGES, gemm::WAVES, gemm::TILE_M>;
+  if constexpr (BITS != 8)
+    if (tall) kern = affine_gemm_kernel<BITS, XT, gemm::KB, gemm::NSTAGES, gemm::WAVES, gemm::TILE_M_TALL>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(64 * gemm::WAVES), 0, s, (const f16_t*)x16,
+                     (const int*)xexp, m, k, packed, (const uint32_t*)sbt, (const int*)wexp, n, G,
+                     (const XT*)bias, (XT*)y);
   return hipGetLastError();
 }
 

@@ -155,6 +155,25 @@ def test_forward_paths_ragged(path, xdt, shape):
     assert_close(y, y_ref, D, K, xdt, label=f"{path} {xdt} {shape}")
 
 
+# enough output columns that the GEMM takes 256-row blocks (two blocks per
+# compute unit; 8-bit codes keep 128-row blocks); M is ragged against 256 and
+# N against 128
+TALL_SHAPES = [(300, 128, 32808, 4, 32), (300, 192, 32808, 2, 64), (260, 128, 32808, 8, 128)]
+
+
+@pytest.mark.parametrize("shape", TALL_SHAPES)
+def test_forward_gemm_tall_blocks_ragged(shape):
+    M, K, N, bits, G = shape
+    inp = workloads.affine_inputs(M, K, N, x_dtype="bf16", bias=True, seed=M + K + N + bits)
+    old = qlq.qlq_get_skinny_max_m()
+    qlq.qlq_set_skinny_max_m(0)
+    try:
+        y, y_ref, D = _forward_case(inp, bits, G, torch.bfloat16)
+    finally:
+        qlq.qlq_set_skinny_max_m(old)
+    assert_close(y, y_ref, D, K, torch.bfloat16, label=f"gemm tall {shape}")
+
+
 def test_forward_flattens_leading_dims():
     inp = workloads.affine_inputs(6, 256, 48, x_dtype="bf16", bias=True, seed=3)
     x = inp["x"].reshape(2, 3, 256).to(dev())
