@@ -53,28 +53,48 @@ __device__ __forceinline__ int floor_log2(float v) {  // v > 0, finite
 }
 
 // ------------------------------------------------------------------ pre-pass
-// Column n: exponent f_n, then the fp16 pair (s', b') of every group, stored
-// group-major (sbt[g * NP + n], NP = N rounded up to 4) so that one k-range's
-// entries for a block of columns are contiguous.
+// Columns n0 .. n0+63 (one 256-thread block): exponent f_n (four threads per
+// column, groups interleaved), then the fp16 pair (s', b') of every group,
+// stored group-major (sbt[g * NP + n], NP = N rounded up to 4) so that a
+// k-range's entries for a block of columns are contiguous; consecutive
+// threads write consecutive columns.
 template <int BITS, typename XT>
-__device__ __forceinline__ void column_exponent(const XT* __restrict__ scales, const XT* __restrict__ biases,
-                                                int n, int ng, int NP, int* __restrict__ wexp,
-                                                uint32_t* __restrict__ sbt) {
+__device__ __forceinline__ void column_block(const XT* __restrict__ scales, const XT* __restrict__ biases,
+                                             int n0, int N, int ng, int* __restrict__ wexp,
+                                             uint32_t* __restrict__ sbt) {
   constexpr float qmax = (float)((1 << BITS) - 1);
-  int f = -1000;
-  for (int g = 0; g < ng; ++g) {
-    const float s = Elem<XT>::load(scales, (int64_t)n * ng + g);
-    const float b = Elem<XT>::load(biases, (int64_t)n * ng + g);
-    const float top = fabsf(b) + qmax * fabsf(s);
-    if (s != 0.0f) f = max(f, floor_log2(fabsf(s)) + 10);
-    if (top != 0.0f) f = max(f, floor_log2(top) - 14);
+  __shared__ int fsh[64];
+  const int tid = threadIdx.x, NP = (N + 3) & ~3;
+  {
+    const int c = tid >> 2, n = n0 + c;
+    int f = -1000;
+    if (n < N) {
+#pragma unroll 4
+      for (int g = tid & 3; g < ng; g += 4) {
+        const float sv = Elem<XT>::load(scales, (int64_t)n * ng + g);
+        const float bv = Elem<XT>::load(biases, (int64_t)n * ng + g);
+        const float top = fabsf(bv) + qmax * fabsf(sv);
+        if (sv != 0.0f) f = max(f, floor_log2(fabsf(sv)) + 10);
+        if (top != 0.0f) f = max(f, floor_log2(top) - 14);
+      }
+    }
+    f = max(f, __shfl_xor(f, 1, kWave));
+    f = max(f, __shfl_xor(f, 2, kWave));
+    f = f == -1000 ? 0 : f;
+    if ((tid & 3) == 0) {
+      fsh[c] = f;
+      if (n < N) wexp[n] = f;
+    }
   }
-  f = f == -1000 ? 0 : f;
-  wexp[n] = f;
-  for (int g = 0; g < ng; ++g) {
-    const float s = Elem<XT>::load(scales, (int64_t)n * ng + g);
-    const float b = Elem<XT>::load(biases, (int64_t)n * ng + g);
-    const f16_t s16 = (f16_t)ldexpf(s, 24 - f), b16 = (f16_t)ldexpf(b, -f);
+  __syncthreads();
+  const int c = tid & 63, n = n0 + c;
+  if (n >= N) return;
+  const int f = fsh[c];
+#pragma unroll 4
+  for (int g = tid >> 6; g < ng; g += 4) {
+    const float sv = Elem<XT>::load(scales, (int64_t)n * ng + g);
+    const float bv = Elem<XT>::load(biases, (int64_t)n * ng + g);
+    const f16_t s16 = (f16_t)ldexpf(sv, 24 - f), b16 = (f16_t)ldexpf(bv, -f);
     sbt[(int64_t)g * NP + n] = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
                                ((uint32_t)__builtin_bit_cast(uint16_t, b16) << 16);
   }
@@ -95,8 +115,7 @@ gemm_prep_wave_kernel(const XT* __restrict__ x, int M, int K, const XT* __restri
   constexpr int G16 = EPT / 16;
   const int row_blocks = (M + 3) / 4;
   if ((int)blockIdx.x >= row_blocks) {
-    const int n = ((int)blockIdx.x - row_blocks) * 256 + threadIdx.x;
-    if (n < N) column_exponent<BITS, XT>(scales, biases, n, K / G, (N + 3) & ~3, wexp, sbt);
+    column_block<BITS, XT>(scales, biases, ((int)blockIdx.x - row_blocks) * 64, N, K / G, wexp, sbt);
     return;
   }
   const int lane = threadIdx.x & 63;
@@ -148,8 +167,7 @@ gemm_prep_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ 
   constexpr int HALF = PER / 2;
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= M) {
-    const int n = ((int)blockIdx.x - M) * 256 + tid;
-    if (n < N) column_exponent<BITS, XT>(scales, biases, n, K / G, (N + 3) & ~3, wexp, sbt);
+    column_block<BITS, XT>(scales, biases, ((int)blockIdx.x - M) * 64, N, K / G, wexp, sbt);
     return;
   }
   __shared__ float red[4];
@@ -504,7 +522,7 @@ static hipError_t gemm_launch(const void* x, int64_t M, int64_t K, const uint32_
   uint32_t* sbt = (uint32_t*)((char*)ws + L.sb);
   const int m = (int)M, n = (int)N, k = (int)K;
   if (K <= 64 * 64) {
-    const unsigned blocks = (unsigned)(cdiv(M, 4) + cdiv(N, 256));
+    const unsigned blocks = (unsigned)(cdiv(M, 4) + cdiv(N, 64));
 #define QLQ_PREP(EPT_)                                                                                  \
   hipLaunchKernelGGL((gemm_prep_wave_kernel<BITS, XT, EPT_>), dim3(blocks), dim3(256), 0, s, (const XT*)x, m, \
                      k, (const XT*)scales, (const XT*)biases, n, G, x16, xexp, wexp, sbt)
@@ -513,7 +531,7 @@ static hipError_t gemm_launch(const void* x, int64_t M, int64_t K, const uint32_
     else QLQ_PREP(64);
 #undef QLQ_PREP
   } else {
-    hipLaunchKernelGGL((gemm_prep_kernel<BITS, XT>), dim3((unsigned)(M + cdiv(N, 256))), dim3(256), 0, s,
+    hipLaunchKernelGGL((gemm_prep_kernel<BITS, XT>), dim3((unsigned)(M + cdiv(N, 64))), dim3(256), 0, s,
                        (const XT*)x, m, k, (const XT*)scales, (const XT*)biases, n, G, x16, xexp, wexp, sbt);
   }
   hipError_t e = hipGetLastError();
