@@ -45,11 +45,13 @@ template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
   static __device__ __forceinline__ void store(bf16_t* p, int64_t i, float v) { p[i] = (bf16_t)f32_to_bf16_rne(v); }
   static __device__ __forceinline__ float round(float v) { return bf16_to_f32(f32_to_bf16_rne(v)); }
+  static __device__ __forceinline__ uint16_t bits(float v) { return (uint16_t)f32_to_bf16_rne(v); }
 };
 template <> struct Elem<f16_t> {
   static __device__ __forceinline__ float load(const f16_t* p, int64_t i) { return (float)p[i]; }
   static __device__ __forceinline__ void store(f16_t* p, int64_t i, float v) { p[i] = (f16_t)v; }
   static __device__ __forceinline__ float round(float v) { return (float)(f16_t)v; }
+  static __device__ __forceinline__ uint16_t bits(float v) { return __builtin_bit_cast(uint16_t, (f16_t)v); }
 };
 
 // 16-bit storage bits -> fp32 value for a 16-bit storage type.
@@ -103,6 +105,45 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
   return v;
+}
+
+// Store a 64x64 tile of outputs held in the 32x32 MFMA result layout (lane l,
+// element e of sub-tile (i, j) is row 32i + 8(e/4) + 4(l/32) + e%4, column
+// 32j + l%32) as 16-bit values at out[row0 + r, col0 + c] (r < nrows, c <
+// ncols, leading dimension ldo).  The values are rounded once, parked in the
+// calling wave's LDS area (64 rows x 144 bytes: the 16-byte pad keeps the two
+// half-waves' writes on different banks) and leave as 16-byte row-contiguous
+// stores where the row is aligned, else element by element.
+constexpr int kTileStageBytes = 64 * 144;
+template <typename OT>
+__device__ __forceinline__ void store_tile64_16(const float (&v)[2][2][16], OT* __restrict__ out, int64_t ldo,
+                                                int row0, int col0, int nrows, int ncols, int8_t* lds, int lane) {
+  constexpr int STRIDE = 144;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3), c = 32 * j + (lane & 31);
+        *reinterpret_cast<uint16_t*>(lds + r * STRIDE + c * 2) = Elem<OT>::bits(v[i][j][e]);
+      }
+  // one wave's LDS accesses complete in order: the reads below see the writes
+  const bool vec = ldo % 8 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = it * 8 + (lane >> 3), c = (lane & 7) * 8;
+    const u32x4_v d = *reinterpret_cast<const u32x4_v*>(lds + r * STRIDE + c * 2);
+    if (r >= nrows || c >= ncols) continue;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(out + (int64_t)(row0 + r) * ldo + col0 + c);
+    if (vec && c + 8 <= ncols) {
+      *reinterpret_cast<u32x4_v*>(dst) = d;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (c + t < ncols) dst[t] = (uint16_t)(d[t >> 1] >> (16 * (t & 1)));
+    }
+  }
 }
 
 // 16 consecutive elements (16-byte aligned) widened to fp32.

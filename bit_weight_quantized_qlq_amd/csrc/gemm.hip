@@ -467,7 +467,8 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
         for (int e = 0; e < 16; ++e) acc[i][j][e] += red[(wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane];
   }
 
-  // ---- epilogue: y = 2^(e_m + f_n) * acc + bias, one rounding
+  // ---- epilogue: y = 2^(e_m + f_n) * acc + bias, one rounding; each wave
+  // stages its rows 64 at a time in its own LDS area and stores them whole
   int fcol[2];
   float bcol[2];
 #pragma unroll
@@ -476,22 +477,28 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
     fcol[j] = wexp[n];
     bcol[j] = bias ? Elem<XT>::load(bias, n) : 0.0f;
   }
+  static_assert(C::KSPLIT == 2 ? kTileStageBytes <= 64 * 64 * 4 : 4 * kTileStageBytes <= C::LDS, "staging fits");
+  if constexpr (C::KSPLIT == 1) __syncthreads();  // every wave is done with the ring
+  int8_t* stage = smem + (C::KSPLIT == 2 ? wq * 64 * 64 * 4 : wid * kTileStageBytes);
+  const int col0 = n_blk + wn * 64;
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  for (int hf = 0; hf < MI / 2; ++hf) {
+    const int row0 = m_blk + wm * (BMT / 2) + 64 * hf;
+    float v[2][2][16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int m = m_blk + wm * (BMT / 2) + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (m >= M) continue;
-      const int em = xexp[m];
+    for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n_blk + wn * 64 + 32 * j + (lane & 31);
-        if (n >= N) continue;
-        float v = ldexpf(acc[i][j][e], em + fcol[j]);
-        if (bias) v = v + bcol[j];
-        Elem<XT>::store(y, (int64_t)m * N + n, v);
+      for (int e = 0; e < 16; ++e) {
+        const int m = row0 + 32 * i2 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int em = m < M ? xexp[m] : 0;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float t = ldexpf(acc[2 * hf + i2][j][e], em + fcol[j]);
+          if (bias) t = t + bcol[j];
+          v[i2][j][e] = t;
+        }
       }
-    }
+    store_tile64_16<XT>(v, y, N, row0, col0, M - row0, N - col0, stage, lane);
   }
 }
 
@@ -536,12 +543,14 @@ static hipError_t gemm_launch(const void* x, int64_t M, int64_t K, const uint32_
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // (8-bit codes: a 256-row stage does not fit twice in a compute unit's LDS)
+  // 4-bit codes only: an 8-bit 256-row stage does not fit twice in a compute
+  // unit's LDS, and the 2-bit decode of a 128x64 wave tile runs out of
+  // registers
   const int64_t tall_tiles = cdiv(M, gemm::TILE_M_TALL) * cdiv(N, gemm::BN);
-  const bool tall = BITS != 8 && tall_tiles >= 2 * 256;
+  const bool tall = BITS == 4 && tall_tiles >= 2 * 256;
   const int64_t tiles = tall ? tall_tiles : cdiv(M, gemm::TILE_M) * cdiv(N, gemm::BN);
   auto kern = affine_gemm_kernel<BITS, XT, gemm::KB, gemm::NSTAGES, gemm::WAVES, gemm::TILE_M>;
-  if constexpr (BITS != 8)
+  if constexpr (BITS == 4)
     if (tall) kern = affine_gemm_kernel<BITS, XT, gemm::KB, gemm::NSTAGES, gemm::WAVES, gemm::TILE_M_TALL>;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(64 * gemm::WAVES), 0, s, (const f16_t*)x16,
                      (const int*)xexp, m, k, packed, (const uint32_t*)sbt, (const int*)wexp, n, G,

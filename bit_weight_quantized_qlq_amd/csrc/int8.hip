@@ -152,6 +152,26 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
   // the zero tiles issued past the end may still be landing in the ring
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  // epilogue operands, loaded before the join so that their latency overlaps it
+  float sam[2][16], sbn[2], bn[2];
+  if constexpr (OUT != 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m_blk + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        sam[i][e] = m < M ? sa[m] : 0.0f;
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = min(n_blk + wn * 64 + 32 * j + (lane & 31), N - 1);
+      sbn[j] = sb[n];
+      bn[j] = !bias ? 0.0f
+                    : OUT == 1 ? Elem<f16_t>::load((const f16_t*)bias, n)
+                               : Elem<bf16_t>::load((const bf16_t*)bias, n);
+    }
+  }
+
   // ---- join the two k-halves: waves 4-7 park their sums in LDS (the tile
   // buffers are free now), waves 0-3 add them and run the epilogue
   int32_t* red = reinterpret_cast<int32_t*>(smem);  // 4 sub-tiles x 64 values x 64 lanes
@@ -173,31 +193,39 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] += red[(wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane];
 
+  if constexpr (OUT == 0) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int m = m_blk + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (m >= M) continue;
-      const float sam = OUT ? sa[m] : 0.0f;
+      for (int e = 0; e < 16; ++e) {
+        const int m = m_blk + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n_blk + wn * 64 + 32 * j + (lane & 31);
-        if (n >= N) continue;
-        if constexpr (OUT == 0) {
-          reinterpret_cast<int32_t*>(out)[(int64_t)m * N + n] = acc[i][j][e];
-        } else {
-          float v = ((float)acc[i][j][e] * sam) * sb[n];
-          if constexpr (OUT == 1) {
-            if (bias) v = v + Elem<f16_t>::load((const f16_t*)bias, n);
-            Elem<f16_t>::store((f16_t*)out, (int64_t)m * N + n, v);
-          } else {
-            if (bias) v = v + Elem<bf16_t>::load((const bf16_t*)bias, n);
-            Elem<bf16_t>::store((bf16_t*)out, (int64_t)m * N + n, v);
-          }
+        for (int j = 0; j < 2; ++j) {
+          const int n = n_blk + wn * 64 + 32 * j + (lane & 31);
+          if (n < N) reinterpret_cast<int32_t*>(out)[(int64_t)m * N + n] = acc[i][j][e];
         }
       }
-    }
+  } else {
+    // y = fp32(c) * sa[m] * sb[n] (+ bias[n]), rounded once; this wave's own
+    // part of the join area (already read) stages the 16-bit tile
+    float v[2][2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          v[i][j][e] = ((float)acc[i][j][e] * sam[i][e]) * sbn[j];
+          if (bias) v[i][j][e] = v[i][j][e] + bn[j];
+        }
+    static_assert(kTileStageBytes <= 64 * 64 * 4, "staging fits the wave's join area");
+    int8_t* stage = smem + wq * 64 * 64 * 4;
+    const int row0 = m_blk + wm * 64, col0 = n_blk + wn * 64;
+    if constexpr (OUT == 1)
+      store_tile64_16<f16_t>(v, (f16_t*)out, N, row0, col0, M - row0, N - col0, stage, lane);
+    else
+      store_tile64_16<bf16_t>(v, (bf16_t*)out, N, row0, col0, M - row0, N - col0, stage, lane);
   }
 }
 

@@ -155,10 +155,11 @@ def test_forward_paths_ragged(path, xdt, shape):
     assert_close(y, y_ref, D, K, xdt, label=f"{path} {xdt} {shape}")
 
 
-# enough output columns that the GEMM takes 256-row blocks (two blocks per
-# compute unit; 8-bit codes keep 128-row blocks); M is ragged against 256 and
-# N against 128
-TALL_SHAPES = [(300, 128, 32808, 4, 32), (300, 192, 32808, 2, 64), (260, 128, 32808, 8, 128)]
+# enough output columns that the GEMM takes 256-row blocks for 4-bit codes
+# (two blocks per compute unit; 2- and 8-bit codes keep 128-row blocks); M is
+# ragged against 256 and N against 128
+TALL_SHAPES = [(300, 128, 32808, 4, 32), (520, 256, 32808, 4, 128), (300, 192, 32808, 2, 64),
+               (260, 128, 32808, 8, 128)]
 
 
 @pytest.mark.parametrize("shape", TALL_SHAPES)
