@@ -206,6 +206,27 @@ hipError_t launch_ternary_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* p
 // One 256-thread block per row.  Pass 1: exact fp32 absmax (block reduction).
 // Pass 2: q = clamp(rint(v / s), -128, 127) with s = a / 127 (1 if 0).
 // Each thread handles 16 consecutive elements per step (K % 16 == 0).
+// x / s rounded to nearest for one divisor s shared by a whole row: the
+// correctly rounded reciprocal y = RN(1/s) once, then per quotient q =
+// RN(x*y), the exact residual r = x - s*q (one fused multiply-add) and
+// RN(q + r*y), which is the correctly rounded quotient when y is the
+// correctly rounded reciprocal and nothing under- or overflows (Markstein's
+// correction step).  Here |x| <= 127 |s|; divisors outside [2^-100, 2^100]
+// keep the full division.
+struct RowDivider {
+  float s, y;
+  bool fast;
+  __device__ __forceinline__ explicit RowDivider(float s_) : s(s_), y(__fdiv_rn(1.0f, s_)) {
+    const float as = fabsf(s_);
+    fast = as >= 0x1p-100f && as <= 0x1p100f;
+  }
+  __device__ __forceinline__ float div(float x) const {
+    if (!fast) return __fdiv_rn(x, s);
+    const float q = x * y;
+    return fmaf(fmaf(-s, q, x), y, q);
+  }
+};
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 quantize_rows_int8_kernel(const T* __restrict__ v, int64_t K, int8_t* __restrict__ q,
@@ -230,6 +251,7 @@ quantize_rows_int8_kernel(const T* __restrict__ v, int64_t K, int8_t* __restrict
   float s = __fdiv_rn(a, 127.0f);
   if (s == 0.0f) s = 1.0f;
   if (tid == 0) scale[row] = s;
+  const RowDivider dv(s);
 
   for (int64_t k = (int64_t)tid * 16; k < K; k += 256 * 16) {
     float e[16];
@@ -240,7 +262,7 @@ quantize_rows_int8_kernel(const T* __restrict__ v, int64_t K, int8_t* __restrict
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float r = rintf(__fdiv_rn(e[4 * i + j], s));
+        float r = rintf(dv.div(e[4 * i + j]));
         r = fminf(fmaxf(r, -128.0f), 127.0f);
         word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
       }
@@ -280,6 +302,7 @@ quantize_rows_int8_wave_kernel(const T* __restrict__ v, int R, int K, int8_t* __
   float s = __fdiv_rn(a, 127.0f);
   if (s == 0.0f) s = 1.0f;
   if (lane == 0) scale[row] = s;
+  const RowDivider dv(s);
 #pragma unroll
   for (int g = 0; g < G16; ++g) {
     if (!in[g]) continue;
@@ -289,7 +312,7 @@ quantize_rows_int8_wave_kernel(const T* __restrict__ v, int R, int K, int8_t* __
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float r = rintf(__fdiv_rn(e[g * 16 + 4 * i + j], s));
+        float r = rintf(dv.div(e[g * 16 + 4 * i + j]));
         r = fminf(fmaxf(r, -128.0f), 127.0f);
         word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
       }
@@ -299,16 +322,75 @@ quantize_rows_int8_wave_kernel(const T* __restrict__ v, int R, int K, int8_t* __
   }
 }
 
+// One 256-thread block per row, EPT elements per thread (16-element groups
+// interleaved across the block: coalesced 16-byte loads and stores); the row
+// stays in registers between the max and the quantization.
+template <typename T, int EPT>
+__global__ void __launch_bounds__(256)
+quantize_rows_int8_block_kernel(const T* __restrict__ v, int K, int8_t* __restrict__ q,
+                                float* __restrict__ scale) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const T* vr = v + row * K;
+  constexpr int G16 = EPT / 16;
+  float e[EPT];
+  bool in[G16];
+#pragma unroll
+  for (int g = 0; g < G16; ++g) {
+    const int k = (g * 256 + tid) * 16;
+    in[g] = k < K;
+    float t[16];
+    load16<T>(vr + (in[g] ? k : 0), t);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[g * 16 + i] = in[g] ? t[i] : 0.0f;
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) a = fmaxf(a, fabsf(e[i]));
+  a = wave_max_dpp(a);
+  if ((tid & 63) == 0) red[tid >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float s = __fdiv_rn(a, 127.0f);
+  if (s == 0.0f) s = 1.0f;
+  if (tid == 0) scale[row] = s;
+  const RowDivider dv(s);
+#pragma unroll
+  for (int g = 0; g < G16; ++g) {
+    if (!in[g]) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float r = rintf(dv.div(e[g * 16 + 4 * i + j]));
+        r = fminf(fmaxf(r, -128.0f), 127.0f);
+        word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
+      }
+      w[i] = word;
+    }
+    *reinterpret_cast<uint4*>(q + row * K + (g * 256 + tid) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 template <typename T>
 static void quant_rows_launch(const void* v, int64_t R, int64_t K, int8_t* q, float* scale, hipStream_t s) {
-  if (K <= 64 * 64) {
-    dim3 grid((unsigned)cdiv(R, 4)), block(256);
-    if (K <= 64 * 16)
-      hipLaunchKernelGGL((quantize_rows_int8_wave_kernel<T, 16>), grid, block, 0, s, (const T*)v, (int)R, (int)K, q, scale);
-    else if (K <= 64 * 32)
-      hipLaunchKernelGGL((quantize_rows_int8_wave_kernel<T, 32>), grid, block, 0, s, (const T*)v, (int)R, (int)K, q, scale);
+  // short rows: a wave per row; up to 16384: a block per row (four times the
+  // waves, so the per-element work spreads over every SIMD); longer: two
+  // passes over the row
+  if (K <= 64 * 16) {
+    hipLaunchKernelGGL((quantize_rows_int8_wave_kernel<T, 16>), dim3((unsigned)cdiv(R, 4)), dim3(256), 0, s,
+                       (const T*)v, (int)R, (int)K, q, scale);
+  } else if (K <= 256 * 64) {
+    dim3 grid((unsigned)R), block(256);
+    if (K <= 256 * 16)
+      hipLaunchKernelGGL((quantize_rows_int8_block_kernel<T, 16>), grid, block, 0, s, (const T*)v, (int)K, q, scale);
+    else if (K <= 256 * 32)
+      hipLaunchKernelGGL((quantize_rows_int8_block_kernel<T, 32>), grid, block, 0, s, (const T*)v, (int)K, q, scale);
     else
-      hipLaunchKernelGGL((quantize_rows_int8_wave_kernel<T, 64>), grid, block, 0, s, (const T*)v, (int)R, (int)K, q, scale);
+      hipLaunchKernelGGL((quantize_rows_int8_block_kernel<T, 64>), grid, block, 0, s, (const T*)v, (int)K, q, scale);
   } else {
     hipLaunchKernelGGL(quantize_rows_int8_kernel<T>, dim3((unsigned)R), dim3(256), 0, s, (const T*)v, K, q, scale);
   }

@@ -25,6 +25,46 @@ def test_quantize_rows_bitexact(vdt, K):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
 
 
+def _all_values_up_to(amax, dt):
+    """Every finite value of dt (f16 or bf16) with |v| <= amax, both signs."""
+    if dt == torch.float16:
+        bits = np.arange(0, 0x7C00, dtype=np.uint16)
+        vals = bits.view(np.float16).astype(np.float32)
+    else:
+        bits = np.arange(0, 0x7F80, dtype=np.uint32)
+        vals = (bits << 16).view(np.float32)
+    vals = vals[vals <= amax]
+    return np.concatenate([vals, -vals[1:]])
+
+
+@pytest.mark.parametrize("vdt", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("amax", [1.0, 0.37890625, 3.140625, 1000.0, 6.103515625e-05])
+def test_quantize_rows_every_value_bitexact(vdt, amax):
+    # each quotient v / (amax / 127) against the oracle's IEEE division: every
+    # representable v up to the row maximum, for the wave-per-row kernel
+    # (rows of 4096) and the block-per-row kernel (one row of 32768)
+    vals = _all_values_up_to(amax, vdt)
+    for K in (4096, 32768):
+        per = K - 1
+        nrows = (len(vals) + per - 1) // per
+        if K == 32768 and nrows > 1:
+            vals_k = vals[:per]
+            nrows = 1
+        else:
+            vals_k = vals
+        rows = np.zeros((nrows, K), dtype=np.float32)
+        rows[:, 0] = amax
+        flat = rows[:, 1:].reshape(-1)
+        flat[: len(vals_k)] = vals_k
+        rows[:, 1:] = flat.reshape(nrows, per)
+        v = torch.from_numpy(rows).to(vdt)
+        assert torch.equal(v.float(), torch.from_numpy(rows)), "values representable"
+        q, sc = qlq.qlq_quantize_rows_int8(v.to(dev()))
+        q_ref, s_ref = oracle.quantize_rows_int8(rows)
+        assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32)), (K, amax)
+        assert np.array_equal(q.cpu().numpy(), q_ref), (K, amax)
+
+
 def test_quantize_rows_workload_bitexact():
     inp = workloads.workload_inputs("w8a8_perchannel")
     q, s = qlq.qlq_quantize_rows_int8(inp["x"].to(dev()))
