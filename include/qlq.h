@@ -110,7 +110,10 @@ QLQ_API int qlq_dequantize(const uint32_t* packed, const void* scales, const voi
 
 /*
  * qlq_linear_workspace_size - bytes of device workspace qlq_linear_forward
- * needs for these arguments (0 when the call takes the skinny path).
+ * needs for these arguments (0 when the call takes the skinny path, or the
+ * arguments are invalid).  GEMM path: x rescaled to fp16 [M, K], per-row and
+ * per-column exponents, and the per-group fp16 (scale, bias) pairs
+ * [K/group_size, round_up(N, 4)].
  */
 QLQ_API size_t qlq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int bits,
                                          int group_size, int x_dtype);
@@ -126,11 +129,17 @@ QLQ_API size_t qlq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int bi
  *   bias    [N] of x_dtype, or NULL.
  *   y       [M, N] of x_dtype (out).  Accumulation is fp32; y is rounded once.
  *   workspace  device memory of at least qlq_linear_workspace_size() bytes,
- *           16-byte aligned; may be NULL when that size is 0.
+ *           256-byte aligned (QLQ_ERR_ALIGNMENT otherwise); may be NULL when
+ *           that size is 0.  The call overwrites it; it holds no state
+ *           between calls, and calls sharing one workspace must be ordered
+ *           on one stream.
  *
  * M <= qlq_get_skinny_max_m() (and every fp32 x) takes the GEMV-shaped skinny
- * kernel; larger M takes the MFMA GEMM.  bits in {2, 4, 8}; group_size in
- * {32, 64, 128}; x_dtype == sb_dtype in {F32, F16, BF16}.
+ * kernel.  Larger M takes the MFMA GEMM when K % 64 == 0, 256*K < 2^31 and
+ * 4*(K/group_size)*round_up(N, 4) < 2^31 (its operands are addressed with
+ * 32-bit buffer offsets); other shapes take the skinny kernel, and
+ * qlq_linear_workspace_size() returns 0 for them.  bits in {2, 4, 8};
+ * group_size in {32, 64, 128}; x_dtype == sb_dtype in {F32, F16, BF16}.
  */
 QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
                                const uint32_t* packed, const void* scales,
@@ -209,7 +218,8 @@ QLQ_API size_t w8a8_workspace_size(int64_t M, int64_t K);
  *
  *   x [M, K] of x_dtype (F16 or BF16); w [N, K] int8; scale_w [N] fp32;
  *   bias [N] of x_dtype or NULL; y [M, N] of x_dtype (out);
- *   workspace >= w8a8_workspace_size(M, K) bytes (holds quant_a(x) and sx).
+ *   workspace >= w8a8_workspace_size(M, K) bytes, 16-byte aligned (holds
+ *   quant_a(x) and sx; overwritten, no state kept between calls).
  *   K % 16 == 0, K <= 131071.
  */
 QLQ_API int w8a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
