@@ -200,6 +200,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void load_lds_b128(__amdgpu_buffer_rsrc_t r, void* dst, int off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
 }
+// Same with a wave-uniform byte offset soff added in the scalar unit (an
+// offset of a whole operand tile, for instance); voff stays per lane.
+__device__ __forceinline__ void load_lds_b128(__amdgpu_buffer_rsrc_t r, void* dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
+}
 
 // LDS rows of CB 16-byte chunks keep chunk c of row r in slot c ^ lds_swz<CB>(r):
 // the chunk-c reads of 8 (or 16) consecutive rows then fall in 8 (16)

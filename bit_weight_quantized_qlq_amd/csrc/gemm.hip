@@ -227,8 +227,12 @@ template <int BITS, int BK, int STAGES, int WV, int BMT> struct Cfg {
   static constexpr int RB = BK * BITS / 8;          // bytes per packed row per k-iteration
   static constexpr int B_CB = RB / 16;              // chunks per packed row
   static constexpr int B_TILE = BN * RB;
-  static constexpr int SB_OFF = A_TILE + B_TILE;
-  static constexpr int STAGE = SB_OFF + U * 1024;
+  // LDS, slot-major within each operand: [A slot 0..S-1][B slot 0..S-1][SB slot 0..S-1],
+  // so that a fragment address is a fixed register plus a constant per slot
+  static constexpr int B_BASE = STAGES * A_TILE;
+  static constexpr int SB_BASE = B_BASE + STAGES * B_TILE;
+  static constexpr int SB_TILE = U * 1024;
+  static constexpr int STAGE = A_TILE + B_TILE + SB_TILE;
   static constexpr int A_RPI = 1024 / A_ROW;        // A rows per wave-wide load
   static constexpr int B_RPI = 1024 / RB;           // B rows per wave-wide load
   static constexpr int A_LOADS = A_TILE / 1024;     // wave-wide loads per stage
@@ -240,7 +244,8 @@ template <int BITS, int BK, int STAGES, int WV, int BMT> struct Cfg {
   static_assert(WV == 4 || WV == 8, "waves");
   static_assert(BMT % 64 == 0 && BMT <= 256 && (KSPLIT == 1 || BMT == 128), "block rows");
   static_assert(A_LOADS % WV == 0 && B_TILE % 1024 == 0, "tile split");
-  static_assert((STAGES - 2) * (LW + 1) < 64, "vmcnt field");
+  static_assert(STAGES == 2, "double buffer: every wait drains this wave's loads");
+  static_assert(BK == 64, "K % 64 == 0 on this path: no k-iteration crosses K");
   static_assert(LDS * (KSPLIT == 1 ? 2 : 1) <= 160 * 1024, "LDS");
 };
 }  // namespace gemm
@@ -281,61 +286,55 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
   const __amdgpu_buffer_rsrc_t rss = make_rsrc(sbt, ng * NP * 4);
 
   // ---- loads of one stage: this wave's A loads, then its share of the B
-  // and SB loads (other-load o goes to wave o % WV)
-  int a_off[C::APW], a_k[C::APW];
+  // and SB loads (other-load o goes to wave o % WV).  Per-lane offsets are
+  // fixed; the k-iteration's offset goes in the scalar offset.  K % 64 == 0,
+  // so no load crosses K; rows past M / N lie past their buffer and read 0.
+  int a_off[C::APW];
 #pragma unroll
   for (int j = 0; j < C::APW; ++j) {
     const int r = (wid * C::APW + j) * C::A_RPI + lane / C::A_CB;
     const int c = (lane % C::A_CB) ^ lds_swz<C::A_CB>(r);
     a_off[j] = r * K * 2 + c * 16;
-    a_k[j] = c * 8;  // first k of the chunk within the k-iteration
   }
   constexpr int OMAX = (C::NO + WV - 1) / WV;
-  int o_off[OMAX], o_k[OMAX];  // B: byte offset and first k; SB: entry offset and first k
+  int o_off[OMAX];  // B: byte offset in the packed rows; SB: byte offset in the table
 #pragma unroll
   for (int t = 0; t < OMAX; ++t) {
     const int o = wid + WV * t;
     o_off[t] = 0;
-    o_k[t] = 0;
     if (o < C::B_LOADS) {
       const int r = o * C::B_RPI + lane / C::B_CB;
       const int c = (lane % C::B_CB) ^ lds_swz<C::B_CB>(r);
       o_off[t] = r * rowb + c * 16;
-      o_k[t] = c * 16 * 8 / BITS;
     } else if (o < C::NO) {
       // sub-block u = o - B_LOADS: lanes 0-31 its first group, lanes 32-63
       // the second one when a sub-block spans two groups (else the first again)
       const int u = o - C::B_LOADS;
-      o_off[t] = n_blk * 4 + (lane & 31) * 16;
-      o_k[t] = u * 64 + (G < 64 ? (lane >> 5) * G : 0);
+      const int gd = ((u * 64) >> lg_g) + (G < 64 ? lane >> 5 : 0);  // group after the iteration's first
+      o_off[t] = (gd * NP + n_blk) * 4 + (lane & 31) * 16;
     }
   }
   const int n_other = C::NO / WV + (wid < C::NO % WV ? 1 : 0);
 
-#define QLQ_ISSUE(T)                                                                              \
+#define QLQ_ISSUE(T, SLOT)                                                                        \
   do {                                                                                            \
     const int k0_ = (T) * BK;                                                                     \
-    int8_t* st_ = smem + ((T) % STAGES) * C::STAGE;                                               \
-    _Pragma("unroll") for (int j = 0; j < C::APW; ++j) {                                          \
-      const int kk_ = k0_ + a_k[j];                                                               \
-      load_lds_b128(rsa, st_ + (wid * C::APW + j) * 1024, kk_ < K ? a_off[j] + k0_ * 2 : kOutOfRange); \
-    }                                                                                             \
+    _Pragma("unroll") for (int j = 0; j < C::APW; ++j)                                            \
+        load_lds_b128(rsa, smem + (SLOT) * C::A_TILE + (wid * C::APW + j) * 1024, a_off[j], k0_ * 2); \
     _Pragma("unroll") for (int t = 0; t < OMAX; ++t) {                                            \
       const int o_ = wid + WV * t;                                                                \
       if (t < n_other) {                                                                          \
-        const int kk_ = k0_ + o_k[t];                                                             \
         if (o_ < C::B_LOADS)                                                                      \
-          load_lds_b128(rsb, st_ + C::A_TILE + o_ * 1024,                                         \
-                        kk_ < K ? o_off[t] + k0_ / PER * 4 : kOutOfRange);                        \
+          load_lds_b128(rsb, smem + C::B_BASE + (SLOT) * C::B_TILE + o_ * 1024, o_off[t], k0_ / PER * 4); \
         else                                                                                      \
-          load_lds_b128(rss, st_ + C::SB_OFF + (o_ - C::B_LOADS) * 1024,                         \
-                        kk_ < K ? o_off[t] + (kk_ >> lg_g) * NP * 4 : kOutOfRange);               \
+          load_lds_b128(rss, smem + C::SB_BASE + (SLOT) * C::SB_TILE + (o_ - C::B_LOADS) * 1024, o_off[t], \
+                        (k0_ >> lg_g) * NP * 4);                                                  \
       }                                                                                           \
     }                                                                                             \
   } while (0)
 
-  // ---- fragment addresses inside a stage.  This wave's k-steps of a
-  // sub-block are s = kh*SPW + sl, sl < SPW.
+  // ---- fragment addresses in slot 0 (slot s adds s times a tile).  This
+  // wave's k-steps of a sub-block are s = kh*SPW + sl, sl < SPW.
   // B: the words of those steps are contiguous: NBW words from byte boff
   constexpr int NBW = BITS == 8 ? 2 * SPW : SPW;
   // SB: 2-bit codes with 32-wide groups change group between steps 1 and 2
@@ -366,9 +365,9 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
       const int cb = (C::RB / C::U / 16) * u + w0 / 4;  // chunk (4 words per chunk)
 #pragma unroll
       for (int q = 0; q < NBR; ++q)
-        boff[i][u][q] = C::A_TILE + rb * C::RB + ((cb + q) ^ lds_swz<C::B_CB>(rb)) * 16 + (w0 % 4) * 4;
+        boff[i][u][q] = C::B_BASE + rb * C::RB + ((cb + q) ^ lds_swz<C::B_CB>(rb)) * 16 + (w0 % 4) * 4;
       const int gi = G < 64 ? (BITS == 2 ? kh : h) : 0;
-      soff[i][u] = C::SB_OFF + u * 1024 + gi * 512 + rb * 4;
+      soff[i][u] = C::SB_BASE + u * 1024 + gi * 512 + rb * 4;
     }
   }
 
@@ -378,71 +377,77 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_v{};
 
-#pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t) QLQ_ISSUE(t);
-  for (int it = 0; it < nk; ++it) {
-    // this wave's loads of tile it have landed once at most the later
-    // STAGES-2 tiles' loads are outstanding; then the barrier
-    if (n_other == C::NO / WV) wait_loads_and_barrier<(STAGES - 2) * C::LW>();
-    else wait_loads_and_barrier<(STAGES - 2) * (C::LW + 1)>();
-    QLQ_ISSUE(it + STAGES - 1);
-    const int8_t* st = smem + (it % STAGES) * C::STAGE;
-#pragma unroll
-    for (int u = 0; u < C::U; ++u) {
-      u32x4_v af[MI][SPW];
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int sl = 0; sl < SPW; ++sl) af[i][sl] = *reinterpret_cast<const u32x4_v*>(st + aoff[i][u][sl]);
-      u32x4_v bq[2][SPW];  // [j][sl]: dequantized B operands
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint32_t e[2];
-        e[0] = *reinterpret_cast<const uint32_t*>(st + soff[j][u]);
-        e[1] = e[0];
-        if constexpr (SB2)
-          if (G < 64) e[1] = *reinterpret_cast<const uint32_t*>(st + soff[j][u] + 512);
-        uint32_t w[NBW];
-        if constexpr (NBW == 2) {
-          const uint2 v = *reinterpret_cast<const uint2*>(st + boff[j][u][0]);
-          w[0] = v.x; w[1] = v.y;
-        } else {
-#pragma unroll
-          for (int q = 0; q < NBR; ++q) {
-            const u32x4_v v = *reinterpret_cast<const u32x4_v*>(st + boff[j][u][q]);
-            w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
-          }
-        }
-#pragma unroll
-        for (int sl = 0; sl < SPW; ++sl) {
-          const uint32_t ee = SB2 && sl >= 2 ? e[1] : e[0];
-          const f16x2_v s2 = __builtin_bit_cast(f16x2_v, (ee & 0xFFFFu) * 0x10001u);
-          const f16x2_v b2 = __builtin_bit_cast(f16x2_v, (ee >> 16) * 0x10001u);
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            uint32_t qd;
-            if constexpr (BITS == 4) qd = (w[sl] >> (4 * p)) & MASK;
-            else if constexpr (BITS == 2) qd = (w[sl] >> (2 * (4 * h + p))) & MASK;
-            else qd = (w[2 * sl + (p >> 1)] >> (8 * (p & 1))) & MASK;
-            bq[j][sl][p] = __builtin_bit_cast(uint32_t,
-                                              __builtin_elementwise_fma(s2, __builtin_bit_cast(f16x2_v, qd), b2));
-          }
-        }
-      }
-#pragma unroll
-      for (int sl = 0; sl < SPW; ++sl)
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_v, af[i][sl]),
-                                                              __builtin_bit_cast(f16x8_v, bq[j][sl]),
-                                                              acc[i][j], 0, 0, 0);
-    }
+#define QLQ_COMPUTE(SLOT)                                                                          \
+  do {                                                                                             \
+    const int8_t* sa_ = smem + (SLOT) * C::A_TILE;                                                 \
+    const int8_t* sb_ = smem + (SLOT) * C::B_TILE;                                                 \
+    const int8_t* ss_ = smem + (SLOT) * C::SB_TILE;                                                \
+    _Pragma("unroll") for (int u = 0; u < C::U; ++u) {                                             \
+      u32x4_v af[MI][SPW];                                                                         \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i)                                               \
+          _Pragma("unroll") for (int sl = 0; sl < SPW; ++sl)                                       \
+              af[i][sl] = *reinterpret_cast<const u32x4_v*>(sa_ + aoff[i][u][sl]);                 \
+      u32x4_v bq[2][SPW]; /* [j][sl]: dequantized B operands */                                    \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                              \
+        uint32_t e[2];                                                                             \
+        e[0] = *reinterpret_cast<const uint32_t*>(ss_ + soff[j][u]);                               \
+        e[1] = e[0];                                                                               \
+        if constexpr (SB2)                                                                         \
+          if (G < 64) e[1] = *reinterpret_cast<const uint32_t*>(ss_ + soff[j][u] + 512);           \
+        uint32_t w[NBW];                                                                           \
+        if constexpr (NBW == 2) {                                                                  \
+          const uint2 v = *reinterpret_cast<const uint2*>(sb_ + boff[j][u][0]);                    \
+          w[0] = v.x; w[1] = v.y;                                                                  \
+        } else {                                                                                   \
+          _Pragma("unroll") for (int q = 0; q < NBR; ++q) {                                        \
+            const u32x4_v v = *reinterpret_cast<const u32x4_v*>(sb_ + boff[j][u][q]);              \
+            w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];       \
+          }                                                                                        \
+        }                                                                                          \
+        _Pragma("unroll") for (int sl = 0; sl < SPW; ++sl) {                                       \
+          const uint32_t ee = SB2 && sl >= 2 ? e[1] : e[0];                                        \
+          const f16x2_v s2 = __builtin_bit_cast(f16x2_v, (ee & 0xFFFFu) * 0x10001u);               \
+          const f16x2_v b2 = __builtin_bit_cast(f16x2_v, (ee >> 16) * 0x10001u);                   \
+          _Pragma("unroll") for (int p = 0; p < 4; ++p) {                                          \
+            uint32_t qd;                                                                           \
+            if constexpr (BITS == 4) qd = (w[sl] >> (4 * p)) & MASK;                               \
+            else if constexpr (BITS == 2) qd = (w[sl] >> (2 * (4 * h + p))) & MASK;                \
+            else qd = (w[2 * sl + (p >> 1)] >> (8 * (p & 1))) & MASK;                              \
+            bq[j][sl][p] = __builtin_bit_cast(                                                     \
+                uint32_t, __builtin_elementwise_fma(s2, __builtin_bit_cast(f16x2_v, qd), b2));     \
+          }                                                                                        \
+        }                                                                                          \
+      }                                                                                            \
+      _Pragma("unroll") for (int sl = 0; sl < SPW; ++sl)                                           \
+          _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
+              _Pragma("unroll") for (int j = 0; j < 2; ++j)                                        \
+                  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(                              \
+                      __builtin_bit_cast(f16x8_v, af[i][sl]), __builtin_bit_cast(f16x8_v, bq[j][sl]), \
+                      acc[i][j], 0, 0, 0);                                                         \
+    }                                                                                              \
+  } while (0)
+
+  // Double buffer, one barrier per k-iteration: wait for this wave's loads
+  // of tile it (the only ones in flight), barrier (everyone's have landed and
+  // everyone is done with the other slot), issue tile it+1 into the other
+  // slot, compute tile it.  Unrolled by the two slots so that every LDS
+  // address above is a constant offset from a fixed register.
+  QLQ_ISSUE(0, 0);
+  int it = 0;
+  for (; it + 1 < nk; it += 2) {
+    wait_loads_and_barrier<0>();
+    QLQ_ISSUE(it + 1, 1);
+    QLQ_COMPUTE(0);
+    wait_loads_and_barrier<0>();
+    if (it + 2 < nk) QLQ_ISSUE(it + 2, 0);
+    QLQ_COMPUTE(1);
+  }
+  if (it < nk) {  // odd nk: slot 0 holds the last tile
+    wait_loads_and_barrier<0>();
+    QLQ_COMPUTE(0);
   }
 #undef QLQ_ISSUE
-  // the zero tiles issued past the end may still be landing in the ring
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef QLQ_COMPUTE
 
   if constexpr (C::KSPLIT == 2) {
     // ---- join the two k-halves: waves 4-7 park their sums in LDS, waves
