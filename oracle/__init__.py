@@ -35,6 +35,7 @@ from .affine import (
 )
 from .ternary import ternary_pack, ternary_unpack, ternary_forward
 from .int8 import quantize_rows_int8, int8_matmul_int32, w8a8_forward
+from .pergroup import quantize_groups_int8, pergroup_forward
 from .tolerance import tolerance, compare
 
 __all__ = [
@@ -54,6 +55,8 @@ __all__ = [
     "quantize_rows_int8",
     "int8_matmul_int32",
     "w8a8_forward",
+    "quantize_groups_int8",
+    "pergroup_forward",
     "tolerance",
     "compare",
 ]
