@@ -53,6 +53,9 @@ SIGNATURES = {
     "qlq_int8_matmul_int32": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "w8a8_workspace_size": (_sz, [_i64, _i64]),
     "w8a8_linear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "qlq_quantize_groups_int8": (_int, [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp]),
+    "pergroup_workspace_size": (_sz, [_i64, _i64]),
+    "pergroup_linear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _int, _vp, _vp, _vp, _sz, _vp]),
     "qlq_device_check": (_int, [_int]),
     "qlq_last_error": (ctypes.c_char_p, []),
     "qlq_version": (ctypes.c_char_p, []),
@@ -260,6 +263,46 @@ def w8a8_linear_forward(x, w, scale_w, bias=None, out=None, workspace=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().w8a8_linear_forward(_ptr(x2), DTYPE_CODE[x.dtype], M, K, _ptr(w), _ptr(scale_w), N,
                                      _ptr(bias), _ptr(out), _ptr(workspace), ws_bytes, _stream(x)))
+    return out.reshape(*x.shape[:-1], N)
+
+
+# --------------------------------------------------------- per-group int8
+def qlq_quantize_groups_int8(w, group_size):
+    """Per-group symmetric int8: w [N, K] -> (q int8 [N, K], scale f32 [K/group_size, N])."""
+    _dev(w, "w", tuple(DTYPE_CODE), 2)
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    s = torch.empty((K // group_size if group_size > 0 else 0, N), dtype=torch.float32, device=w.device)
+    _check(lib().qlq_quantize_groups_int8(_ptr(w), DTYPE_CODE[w.dtype], N, K, group_size, _ptr(q), _ptr(s),
+                                          _stream(w)))
+    return q, s
+
+
+def pergroup_workspace_size(M, K):
+    return int(lib().pergroup_workspace_size(M, K))
+
+
+def pergroup_linear_forward(x, w, scale_w, group_size, bias=None, out=None, workspace=None):
+    """Per-group int8 linear; M == 1 keeps x in floating point, M > 1 quantizes it."""
+    _dev(x, "x", (torch.float16, torch.bfloat16))
+    _dev(w, "w", torch.int8, 2)
+    _dev(scale_w, "scale_w", torch.float32, 2)
+    if bias is not None:
+        _dev(bias, "bias", x.dtype, 1)
+    x2 = _flatten(x)
+    M, K = x2.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _dev(out, "out", x.dtype)
+    need = pergroup_workspace_size(M, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pergroup_linear_forward(_ptr(x2), DTYPE_CODE[x.dtype], M, K, _ptr(w), _ptr(scale_w), N,
+                                         group_size, _ptr(bias), _ptr(out), _ptr(workspace), ws_bytes,
+                                         _stream(x)))
     return out.reshape(*x.shape[:-1], N)
 
 

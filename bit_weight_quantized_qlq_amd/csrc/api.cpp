@@ -323,4 +323,62 @@ QLQ_API int w8a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K
   return hip_status(qlq::launch_int8_gemm(xq, w, M, N, K, sx, scale_w, bias, x_dtype, y, s), "int8 gemm");
 }
 
+QLQ_API int qlq_quantize_groups_int8(const void* w, int w_dtype, int64_t N, int64_t K, int group_size,
+                                     int8_t* q, float* scale, void* stream) {
+  QLQ_REQUIRE(w && q && scale, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(N >= 0 && N < kMaxDim && K >= 1 && K < kMaxDim, QLQ_ERR_INVALID_ARG, "invalid shape");
+  QLQ_REQUIRE(group_size == 64 || group_size == 128 || group_size == 256, QLQ_ERR_UNSUPPORTED,
+              "group_size=%d not built (64, 128, 256)", group_size);
+  QLQ_REQUIRE(K % group_size == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of group_size=%d",
+              (long long)K, group_size);
+  QLQ_REQUIRE(dtype_ok(w_dtype), QLQ_ERR_UNSUPPORTED, "w_dtype %d", w_dtype);
+  QLQ_REQUIRE(aligned(w, 16) && aligned(q, 16) && aligned(scale, 4), QLQ_ERR_ALIGNMENT, "misaligned pointer");
+  if (N == 0) return ok();
+  if (int st = current_device_status()) return st;
+  return hip_status(qlq::launch_quantize_groups_int8(w, w_dtype, N, K, group_size, q, scale, (hipStream_t)stream),
+                    "quantize groups");
+}
+
+QLQ_API size_t pergroup_workspace_size(int64_t M, int64_t K) {
+  if (M <= 1 || K <= 0) return 0;  // M == 1 keeps x in floating point
+  return w8a8_workspace_size(M, K);
+}
+
+QLQ_API int pergroup_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* w,
+                                    const float* scale_w, int64_t N, int group_size, const void* bias, void* y,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  QLQ_REQUIRE(x && w && scale_w && y, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(M >= 0 && M < kMaxDim && N >= 1 && N < kMaxDim && K >= 1, QLQ_ERR_INVALID_ARG, "invalid shape");
+  QLQ_REQUIRE(group_size == 64 || group_size == 128 || group_size == 256, QLQ_ERR_UNSUPPORTED,
+              "group_size=%d not built (64, 128, 256)", group_size);
+  QLQ_REQUIRE(K % group_size == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of group_size=%d",
+              (long long)K, group_size);
+  QLQ_REQUIRE(x_dtype == QLQ_F16 || x_dtype == QLQ_BF16, QLQ_ERR_UNSUPPORTED, "x_dtype must be F16 or BF16");
+  QLQ_REQUIRE(K <= 131071, QLQ_ERR_UNSUPPORTED, "K=%lld could overflow int32", (long long)K);
+  QLQ_REQUIRE(M != 1 || K <= qlq::kPergroupMvMaxK, QLQ_ERR_UNSUPPORTED,
+              "K=%lld above %lld for the M == 1 product", (long long)K, (long long)qlq::kPergroupMvMaxK);
+  QLQ_REQUIRE(aligned(x, 16) && aligned(w, 16) && aligned(scale_w, 4) && aligned(y, 2) &&
+                  (!bias || aligned(bias, 2)),
+              QLQ_ERR_ALIGNMENT, "misaligned pointer");
+  QLQ_REQUIRE((M + 127) / 128 <= 65535, QLQ_ERR_UNSUPPORTED, "M too large for one launch");
+  if (M == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  if (M == 1) {
+    if (int st = current_device_status()) return st;
+    return hip_status(qlq::launch_pergroup_mv(x, x_dtype, K, w, scale_w, N, group_size, bias, y, s),
+                      "per-group matrix-vector product");
+  }
+  const size_t need = pergroup_workspace_size(M, K);
+  QLQ_REQUIRE(workspace && workspace_bytes >= need, QLQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+              need, workspace ? workspace_bytes : (size_t)0);
+  QLQ_REQUIRE(aligned(workspace, 16), QLQ_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+  if (int st = current_device_status()) return st;
+  int8_t* xq = (int8_t*)workspace;
+  float* sx = (float*)((char*)workspace + (((size_t)M * (size_t)K + 255) & ~(size_t)255));
+  if (int st = hip_status(qlq::launch_quantize_rows_int8(x, x_dtype, M, K, xq, sx, s), "activation quant"))
+    return st;
+  return hip_status(qlq::launch_int8_gemm_pergroup(xq, w, M, N, K, sx, scale_w, group_size, bias, x_dtype, y, s),
+                    "per-group int8 gemm");
+}
+
 }  // extern "C"

@@ -63,13 +63,23 @@ __device__ __forceinline__ i32x16_v mma_i8(u32x4_v a, u32x4_v b, i32x16_v c) {
 // have, and every wave has finished reading slot (it-1) % STAGES), issue the
 // loads of tile it+STAGES-1 into that slot, compute tile it.  Tiles past the
 // last one load as zeros and are never computed.
-template <int OUT, int BK, int STAGES>
+//
+// PG > 0 (per-group weights, group of PG input values): sb is the per-group
+// scale table [K/PG, N]; the int32 accumulators are flushed into fp32 as
+// acc * sb[g, n] at every group boundary of a wave's k-steps (a group longer
+// than a wave's half of an iteration is flushed once per half: the scale is
+// the same, the sum is linear), and y = acc_f * sa[m] (+ bias).  The int32
+// partial of one flush is below 2^24, so its conversion is exact.
+template <int OUT, int BK, int STAGES, int PG = 0>
 __global__ void __launch_bounds__(i8::THREADS, 1)
 int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int M, int N, int K,
                  const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
                  void* __restrict__ out) {
   using namespace i8;
   using C = Cfg<BK, STAGES>;
+  static_assert(PG == 0 || (OUT != 0 && PG % KS == 0), "per-group scales need a scaled output");
+  constexpr int FS = PG == 0 ? C::QN : (PG / KS < C::QN ? PG / KS : C::QN);  // k-steps per flush
+  constexpr int NF = C::QN / FS;                                              // flushes per k-iteration
   // the ring during the K loop, then the 64 KiB of int32 partial sums that
   // join the two k-halves
   __shared__ __attribute__((aligned(16))) int8_t smem[STAGES * C::STAGE];
@@ -120,10 +130,18 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
   }
 
   i32x16_v acc[2][2];
+  f32x16_v accf[2][2];  // per-group mode: rescaled sums
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = i32x16_v{};
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = i32x16_v{};
+      accf[i][j] = f32x16_v{};
+    }
+  int ncol[2];  // this lane's output columns (clamped)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) ncol[j] = min(n_blk + wn * 64 + 32 * j + (lane & 31), N - 1);
+  const int ng = PG ? K / (PG ? PG : 1) : 1;
 
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t) QLQ_ISSUE(t);
@@ -131,6 +149,17 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
     // this thread's loads of tile it are done when at most the later
     // STAGES-2 tiles' loads are outstanding; then the barrier
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(C::VMCNT) : "memory");
+    // per-group scales of this iteration's flushes, requested before the
+    // tile loads so that waiting for them does not wait for those
+    float scf[NF][2];
+    if constexpr (PG != 0) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int g = min((it * BK + (kh * C::QN + f * FS) * KS) / PG, ng - 1);  // past K: zero sums
+#pragma unroll
+        for (int j = 0; j < 2; ++j) scf[f][j] = sb[(int64_t)g * N + ncol[j]];
+      }
+    }
     QLQ_ISSUE(it + STAGES - 1);
     const int8_t* st_ = smem + (it % STAGES) * C::STAGE;
     u32x4_v af[2][C::QN], bf[2][C::QN];
@@ -142,11 +171,25 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
         bf[i][q] = *reinterpret_cast<const u32x4_v*>(st_ + boff[i][q]);
       }
 #pragma unroll
-    for (int q = 0; q < C::QN; ++q)
+    for (int q = 0; q < C::QN; ++q) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mma_i8(af[i][q], bf[j][q], acc[i][j]);
+      if constexpr (PG != 0) {
+        if ((q + 1) % FS == 0) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e)
+                accf[i][j][e] = __builtin_fmaf((float)acc[i][j][e], scf[q / FS][j], accf[i][j][e]);
+              acc[i][j] = i32x16_v{};
+            }
+        }
+      }
+    }
   }
 #undef QLQ_ISSUE
   // the zero tiles issued past the end may still be landing in the ring
@@ -165,7 +208,7 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = min(n_blk + wn * 64 + 32 * j + (lane & 31), N - 1);
-      sbn[j] = sb[n];
+      sbn[j] = PG == 0 ? sb[n] : 1.0f;
       bn[j] = !bias ? 0.0f
                     : OUT == 1 ? Elem<f16_t>::load((const f16_t*)bias, n)
                                : Elem<bf16_t>::load((const bf16_t*)bias, n);
@@ -175,6 +218,7 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
   // ---- join the two k-halves: waves 4-7 park their sums in LDS (the tile
   // buffers are free now), waves 0-3 add them and run the epilogue
   int32_t* red = reinterpret_cast<int32_t*>(smem);  // 4 sub-tiles x 64 values x 64 lanes
+  float* redf = reinterpret_cast<float*>(smem);      // the same area, per-group mode
   __syncthreads();
   if (kh == 1) {
 #pragma unroll
@@ -182,7 +226,11 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) red[(wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane] = acc[i][j][e];
+        for (int e = 0; e < 16; ++e) {
+          const int ix = (wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane;
+          if constexpr (PG == 0) red[ix] = acc[i][j][e];
+          else redf[ix] = accf[i][j][e];
+        }
   }
   __syncthreads();
   if (kh == 1) return;
@@ -191,7 +239,11 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] += red[(wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane];
+      for (int e = 0; e < 16; ++e) {
+        const int ix = (wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane;
+        if constexpr (PG == 0) acc[i][j][e] += red[ix];
+        else accf[i][j][e] += redf[ix];
+      }
 
   if constexpr (OUT == 0) {
 #pragma unroll
@@ -207,8 +259,9 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
         }
       }
   } else {
-    // y = fp32(c) * sa[m] * sb[n] (+ bias[n]), rounded once; this wave's own
-    // part of the join area (already read) stages the 16-bit tile
+    // y = fp32(c) * sa[m] * sb[n] (+ bias[n]), or acc_f * sa[m] (+ bias[n])
+    // per group, rounded once; this wave's own part of the join area
+    // (already read) stages the 16-bit tile
     float v[2][2][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -216,7 +269,8 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          v[i][j][e] = ((float)acc[i][j][e] * sam[i][e]) * sbn[j];
+          if constexpr (PG == 0) v[i][j][e] = ((float)acc[i][j][e] * sam[i][e]) * sbn[j];
+          else v[i][j][e] = accf[i][j][e] * sam[i][e];
           if (bias) v[i][j][e] = v[i][j][e] + bn[j];
         }
     static_assert(kTileStageBytes <= 64 * 64 * 4, "staging fits the wave's join area");
@@ -242,6 +296,26 @@ hipError_t launch_int8_gemm_cfg(const int8_t* a, const int8_t* b, int64_t M, int
     hipLaunchKernelGGL((int8_gemm_kernel<1, BK, STAGES>), grid, block, 0, s, a, b, m, n, k, sa, sb, bias, out);
   else
     hipLaunchKernelGGL((int8_gemm_kernel<2, BK, STAGES>), grid, block, 0, s, a, b, m, n, k, sa, sb, bias, out);
+  return hipGetLastError();
+}
+
+// Per-group weights (group_size 64, 128 or 256): scale_w [K/group_size, N].
+hipError_t launch_int8_gemm_pergroup(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K,
+                                     const float* sa, const float* scale_w, int group_size,
+                                     const void* bias, int out_dtype, void* out, hipStream_t s) {
+  const int64_t tiles = cdiv(M, i8::BM) * cdiv(N, i8::BN);
+  dim3 grid((unsigned)tiles), block(i8::THREADS);
+  const int m = (int)M, n = (int)N, k = (int)K;
+#define QLQ_PG_LAUNCH(OUTV, PGV)                                                                       \
+  hipLaunchKernelGGL((int8_gemm_kernel<OUTV, 256, 2, PGV>), grid, block, 0, s, a, b, m, n, k, sa, scale_w, \
+                     bias, out)
+  const bool h = out_dtype == F16;
+  switch (group_size) {
+    case 64: if (h) QLQ_PG_LAUNCH(1, 64); else QLQ_PG_LAUNCH(2, 64); break;
+    case 128: if (h) QLQ_PG_LAUNCH(1, 128); else QLQ_PG_LAUNCH(2, 128); break;
+    default: if (h) QLQ_PG_LAUNCH(1, 256); else QLQ_PG_LAUNCH(2, 256); break;
+  }
+#undef QLQ_PG_LAUNCH
   return hipGetLastError();
 }
 

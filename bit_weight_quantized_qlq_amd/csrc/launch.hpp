@@ -44,5 +44,17 @@ hipError_t launch_ternary_forward(const void* x, int x_dtype, int64_t M, int64_t
 hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K,
                             const float* sa, const float* sb, const void* bias, int out_dtype,
                             void* out, hipStream_t s);
+hipError_t launch_int8_gemm_pergroup(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K,
+                                     const float* sa, const float* scale_w, int group_size,
+                                     const void* bias, int out_dtype, void* out, hipStream_t s);
+
+// pack.hip (per-group weights)
+hipError_t launch_quantize_groups_int8(const void* w, int w_dtype, int64_t N, int64_t K, int group_size,
+                                       int8_t* q, float* scale, hipStream_t s);
+
+// pergroup.hip
+constexpr int64_t kPergroupMvMaxK = 16384;
+hipError_t launch_pergroup_mv(const void* x, int x_dtype, int64_t K, const int8_t* w, const float* scale,
+                              int64_t N, int group_size, const void* bias, void* y, hipStream_t s);
 
 }  // namespace qlq

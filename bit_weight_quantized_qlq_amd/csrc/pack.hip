@@ -375,6 +375,73 @@ quantize_rows_int8_block_kernel(const T* __restrict__ v, int K, int8_t* __restri
   }
 }
 
+// Per-group symmetric int8 quantization: w [N, K] -> q [N, K] int8 and
+// scale [K/G, N] fp32 (group-major).  One wave per (row, 1024-element
+// chunk): lane l holds elements 16l .. 16l+15 of the chunk, so a group is G/16
+// consecutive lanes and its absmax is a shuffle reduction over them.  Same
+// rule as the row quantizer, per group.
+template <typename T, int G>
+__global__ void __launch_bounds__(256)
+quantize_groups_int8_kernel(const T* __restrict__ w, int N, int K, int8_t* __restrict__ q,
+                            float* __restrict__ scale) {
+  static_assert(G % 16 == 0 && 1024 % G == 0 && G / 16 <= 64, "group shape");
+  const int lane = threadIdx.x & 63;
+  const int chunks = (K + 1023) / 1024;
+  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wv >= (int64_t)N * chunks) return;
+  const int n = (int)(wv / chunks), ch = (int)(wv % chunks);
+  const int k = ch * 1024 + lane * 16;
+  const bool in = k < K;
+  float e[16];
+  load16<T>(w + (int64_t)n * K + (in ? k : 0), e);
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, in ? fabsf(e[i]) : 0.0f);
+#pragma unroll
+  for (int o = 1; o < G / 16; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
+  float s = __fdiv_rn(a, 127.0f);
+  if (s == 0.0f) s = 1.0f;
+  if (!in) return;
+  if (lane % (G / 16) == 0) scale[(int64_t)(k / G) * N + n] = s;
+  const RowDivider dv(s);
+  uint32_t wd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float r = rintf(dv.div(e[4 * i + j]));
+      r = fminf(fmaxf(r, -128.0f), 127.0f);
+      word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
+    }
+    wd[i] = word;
+  }
+  *reinterpret_cast<uint4*>(q + (int64_t)n * K + k) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+}
+
+template <typename T>
+static void quant_groups_launch(const void* w, int64_t N, int64_t K, int G, int8_t* q, float* scale,
+                                hipStream_t s) {
+  const dim3 grid((unsigned)cdiv(N * cdiv(K, 1024), 4)), block(256);
+  const int n = (int)N, k = (int)K;
+  if (G == 64)
+    hipLaunchKernelGGL((quantize_groups_int8_kernel<T, 64>), grid, block, 0, s, (const T*)w, n, k, q, scale);
+  else if (G == 128)
+    hipLaunchKernelGGL((quantize_groups_int8_kernel<T, 128>), grid, block, 0, s, (const T*)w, n, k, q, scale);
+  else
+    hipLaunchKernelGGL((quantize_groups_int8_kernel<T, 256>), grid, block, 0, s, (const T*)w, n, k, q, scale);
+}
+
+hipError_t launch_quantize_groups_int8(const void* w, int w_dtype, int64_t N, int64_t K, int group_size,
+                                       int8_t* q, float* scale, hipStream_t s) {
+  switch (w_dtype) {
+    case F32: quant_groups_launch<float>(w, N, K, group_size, q, scale, s); break;
+    case BF16: quant_groups_launch<bf16_t>(w, N, K, group_size, q, scale, s); break;
+    default: quant_groups_launch<f16_t>(w, N, K, group_size, q, scale, s); break;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 static void quant_rows_launch(const void* v, int64_t R, int64_t K, int8_t* q, float* scale, hipStream_t s) {
   // short rows: a wave per row; up to 16384: a block per row (four times the

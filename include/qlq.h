@@ -228,6 +228,46 @@ QLQ_API int w8a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K
                                 size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Per-group int8 weights ("cider/ops.py": pergroup_linear)
+ * ------------------------------------------------------------------------ */
+
+/*
+ * qlq_quantize_groups_int8 - per-group symmetric int8 quantization of
+ * w [N, K] (w_dtype F32, F16 or BF16): every group of group_size consecutive
+ * input values of a row follows the rule of qlq_quantize_rows_int8 (fp32
+ * absmax/127, 1 if 0, q = clamp(rint(w/s), -128, 127)).  q [N, K] int8 and
+ * scale [K/group_size, N] fp32 (out; group-major, the transposed layout of
+ * pergroup_linear).  group_size in {64, 128, 256}, K % group_size == 0.
+ */
+QLQ_API int qlq_quantize_groups_int8(const void* w, int w_dtype, int64_t N, int64_t K,
+                                     int group_size, int8_t* q, float* scale, void* stream);
+
+/* Bytes of workspace pergroup_linear_forward needs: 0 for M == 1, else as
+ * w8a8_workspace_size (quant_a(x) and its row scales). */
+QLQ_API size_t pergroup_workspace_size(int64_t M, int64_t K);
+
+/*
+ * pergroup_linear_forward - per-group int8 linear (pergroup_linear).
+ *   M > 1:  y = sx[m] * sum_g scale_w[g, n] * (sum_{k in g} xq[m, k] w[n, k])
+ *           (+ bias[n]) with xq, sx = quant_a(x) as in w8a8_linear_forward;
+ *           int32 per group, rescaled in fp32, rounded once to x_dtype.
+ *   M == 1: y = sum_k x[k] * w[n, k] * scale_w[g(k), n] (+ bias[n]) with x as
+ *           stored (no activation quantization), fp32 accumulation.
+ *
+ *   x [M, K] of x_dtype (F16 or BF16); w [N, K] int8; scale_w [K/group_size,
+ *   N] fp32; bias [N] of x_dtype or NULL; y [M, N] of x_dtype (out);
+ *   workspace >= pergroup_workspace_size(M, K) bytes, 16-byte aligned, may be
+ *   NULL when that is 0 (overwritten, no state kept between calls).
+ *   group_size in {64, 128, 256}; K % group_size == 0; K <= 131071, and
+ *   K <= 16384 when M == 1 (x is staged whole on chip): else
+ *   QLQ_ERR_UNSUPPORTED.
+ */
+QLQ_API int pergroup_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
+                                    const int8_t* w, const float* scale_w, int64_t N,
+                                    int group_size, const void* bias, void* y, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Device and error reporting
  * ------------------------------------------------------------------------ */
 

@@ -163,3 +163,37 @@ def test_valid_call_without_device_reports_device_error():
     assert _lin() == qlq.QLQ_ERR_DEVICE
     assert qlq.lib().qlq_device_check(0) == qlq.QLQ_ERR_DEVICE
     assert "device" in qlq.last_error()
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, qlq.QLQ_F32, 8, 128, 64, A, B, None), qlq.QLQ_ERR_INVALID_ARG),
+    ((A, qlq.QLQ_F32, 8, 128, 32, A, B, None), qlq.QLQ_ERR_UNSUPPORTED),    # group 32 not built
+    ((A, qlq.QLQ_F32, 8, 192, 128, A, B, None), qlq.QLQ_ERR_INVALID_ARG),   # K % G
+    ((A, 9, 8, 128, 64, A, B, None), qlq.QLQ_ERR_UNSUPPORTED),
+    ((ODD, qlq.QLQ_F32, 8, 128, 64, A, B, None), qlq.QLQ_ERR_ALIGNMENT),
+])
+def test_quantize_groups_validation(args, code):
+    assert qlq.lib().qlq_quantize_groups_int8(*args) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), qlq.QLQ_ERR_INVALID_ARG),
+    (dict(G=32), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(K=320, G=128), qlq.QLQ_ERR_INVALID_ARG),          # K % G
+    (dict(x_dtype=qlq.QLQ_F32), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(M=1, K=32768), qlq.QLQ_ERR_UNSUPPORTED),           # float-x product stages x on chip
+    (dict(ws=None, ws_bytes=0), qlq.QLQ_ERR_WORKSPACE),      # M > 1 quantizes x into the workspace
+    (dict(x=ODD), qlq.QLQ_ERR_ALIGNMENT),
+])
+def test_pergroup_forward_validation(kw, code):
+    a = dict(x=A, x_dtype=qlq.QLQ_F16, M=4, K=256, w=A, s=B, N=32, G=64, bias=None, y=A, ws=B, ws_bytes=1 << 20)
+    a.update(kw)
+    r = qlq.lib().pergroup_linear_forward(a["x"], a["x_dtype"], a["M"], a["K"], a["w"], a["s"], a["N"], a["G"],
+                                          a["bias"], a["y"], a["ws"], a["ws_bytes"], None)
+    assert r == code
+
+
+def test_pergroup_workspace_sizes():
+    L = qlq.lib()
+    assert L.pergroup_workspace_size(1, 4096) == 0
+    assert L.pergroup_workspace_size(2, 4096) == L.w8a8_workspace_size(2, 4096) > 0
