@@ -52,20 +52,30 @@ def test_forward_ragged(xdt, shape):
 
 
 def test_forward_float_branch_full_size():
-    # M == 1 at the decode size: x stays in floating point
-    y, y_ref, D = _case(1, 4096, 4096, 128, torch.float16, seed=51, bias=False)
-    assert_close(y, y_ref, D, 4096, torch.float16, strict=True, label="pergroup M=1 4096")
+    # the workload's single-token case: M == 1 keeps x in floating point
+    name = "pergroup_int8_g128"
+    cfg = workloads.WORKLOADS[name]
+    K, N, G = cfg["K"], cfg["N"], cfg["group_size"]
+    inp = workloads.workload_inputs(name, M=1)
+    q, s = qlq.qlq_quantize_groups_int8(inp["w"].to(dev()), G)
+    y = qlq.pergroup_linear_forward(inp["x"].to(dev()), q, s, G)
+    q_ref, s_ref = oracle.quantize_groups_int8(inp["w"].numpy(), G)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    y_ref, D = oracle.pergroup_forward(f32(inp["x"]), q_ref, s_ref, G)
+    assert_close(y, y_ref, D, K, torch.float16, strict=True, label=f"{name} M=1")
 
 
 def test_forward_quantized_branch_sampled_rows():
-    M, K, N, G = 1024, 4096, 4096, 128
-    inp = workloads.w8a8_inputs(M, K, N, x_dtype="f16", seed=52)
+    name = "pergroup_int8_g128"
+    cfg = workloads.WORKLOADS[name]
+    M, K, G = cfg["M"], cfg["K"], cfg["group_size"]
+    inp = workloads.workload_inputs(name)
     q, s = qlq.qlq_quantize_groups_int8(inp["w"].to(dev()), G)
     y = qlq.pergroup_linear_forward(inp["x"].to(dev()), q, s, G)
     rows = sorted(set([0, 127, 128, 1023] + list(np.random.default_rng(5).choice(M, 12, replace=False))))
     y_ref, D = oracle.pergroup_forward(f32(inp["x"])[rows], q.cpu().numpy(), s.cpu().numpy(), G)
     assert_close(y[torch.as_tensor(rows, device=y.device)], y_ref, D, K, torch.float16, strict=True,
-                 label="pergroup M=1024 sampled rows")
+                 label=f"{name} sampled rows")
 
 
 def test_zero_input_gives_bias():

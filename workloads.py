@@ -20,8 +20,12 @@ round-to-nearest-even conversion):
   w8a8_perchannel     x f16 [1024,4096] ~N(0,1), exactly round(0.001*M*K)
                       distinct positions multiplied by 20 before the cast;
                       W f32 [4096,4096] ~N(0,0.02); no bias
+  pergroup_int8_g128  the w8a8_perchannel recipe (x f16 [1024,4096] with the
+                      same outliers, W f32 [4096,4096] ~N(0,0.02), no bias);
+                      weights quantized per group of 128; its single-token
+                      case draws x [1,4096] by the same recipe
 
-The default seed of a workload is 1000 + its index in the list above (1..5).
+The default seed of a workload is 1000 + its index in the list above (1..6).
 Smaller parity cases reuse the same recipes at other shapes and seeds.
 """
 
@@ -44,6 +48,9 @@ WORKLOADS = {
     "w8a8_perchannel": dict(index=5, kind="w8a8", M=1024, K=4096, N=4096,
                             x_dtype="f16", bias=False, outlier_frac=0.001,
                             outlier_mult=20.0),
+    "pergroup_int8_g128": dict(index=6, kind="w8a8", M=1024, K=4096, N=4096,
+                               group_size=128, x_dtype="f16", bias=False,
+                               outlier_frac=0.001, outlier_mult=20.0),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
