@@ -36,6 +36,7 @@ from .affine import (
 from .ternary import ternary_pack, ternary_unpack, ternary_forward
 from .int8 import quantize_rows_int8, int8_matmul_int32, w8a8_forward
 from .pergroup import quantize_groups_int8, pergroup_forward
+from .w4a8 import pack_weight_int4, unpack_weight_int4, w4a8_forward
 from .tolerance import tolerance, compare
 
 __all__ = [
@@ -57,6 +58,9 @@ __all__ = [
     "w8a8_forward",
     "quantize_groups_int8",
     "pergroup_forward",
+    "pack_weight_int4",
+    "unpack_weight_int4",
+    "w4a8_forward",
     "tolerance",
     "compare",
 ]

@@ -24,8 +24,12 @@ round-to-nearest-even conversion):
                       same outliers, W f32 [4096,4096] ~N(0,0.02), no bias);
                       weights quantized per group of 128; its single-token
                       case draws x [1,4096] by the same recipe
+  w4a8_perchannel     x f16 [1024,4096] by the w8a8_perchannel recipe (same
+                      outlier count and factor); W f32 [K=4096, N=4096]
+                      ~N(0,0.02) drawn in the [K, N] orientation the int4
+                      packer takes; no bias
 
-The default seed of a workload is 1000 + its index in the list above (1..6).
+The default seed of a workload is 1000 + its index in the list above (1..7).
 Smaller parity cases reuse the same recipes at other shapes and seeds.
 """
 
@@ -51,6 +55,9 @@ WORKLOADS = {
     "pergroup_int8_g128": dict(index=6, kind="w8a8", M=1024, K=4096, N=4096,
                                group_size=128, x_dtype="f16", bias=False,
                                outlier_frac=0.001, outlier_mult=20.0),
+    "w4a8_perchannel": dict(index=7, kind="w4a8", M=1024, K=4096, N=4096,
+                            x_dtype="f16", bias=False, outlier_frac=0.001,
+                            outlier_mult=20.0),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -119,6 +126,28 @@ def w8a8_inputs(M, K, N, x_dtype="f16", bias=False, seed=0, outlier_frac=0.001,
     }
 
 
+def w4a8_inputs(M, K, N, x_dtype="f16", bias=False, seed=0, outlier_frac=0.001,
+                outlier_mult=20.0, w_std=0.02, bias_std=0.01):
+    """x [M,K] with outliers, W [K,N] fp32 (the int4 packer's orientation),
+    optional bias [N]."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    w = (rng.standard_normal((K, N), dtype=np.float32) * np.float32(w_std)).astype(np.float32)
+    b = None
+    if bias:
+        b = (rng.standard_normal(N, dtype=np.float32) * np.float32(bias_std)).astype(np.float32)
+    n_out = int(round(outlier_frac * M * K))
+    if n_out:
+        pos = rng.choice(M * K, n_out, replace=False)
+        flat = x.reshape(-1)
+        flat[pos] = flat[pos] * np.float32(outlier_mult)
+    return {
+        "x": _cast(x, x_dtype),
+        "w": torch.from_numpy(w),
+        "bias": None if b is None else _cast(b, x_dtype),
+    }
+
+
 def workload_inputs(name, seed=None, **shape):
     """Inputs of a named workload; ``shape`` may override M, K, N."""
     cfg = dict(WORKLOADS[name])
@@ -132,6 +161,10 @@ def workload_inputs(name, seed=None, **shape):
                               weight_scale=cfg["weight_scale"], bias=cfg["bias"], seed=seed)
     if cfg["kind"] == "w8a8":
         return w8a8_inputs(cfg["M"], cfg["K"], cfg["N"], x_dtype=cfg["x_dtype"],
+                           bias=cfg["bias"], seed=seed, outlier_frac=cfg["outlier_frac"],
+                           outlier_mult=cfg["outlier_mult"])
+    if cfg["kind"] == "w4a8":
+        return w4a8_inputs(cfg["M"], cfg["K"], cfg["N"], x_dtype=cfg["x_dtype"],
                            bias=cfg["bias"], seed=seed, outlier_frac=cfg["outlier_frac"],
                            outlier_mult=cfg["outlier_mult"])
     raise ValueError(cfg["kind"])
