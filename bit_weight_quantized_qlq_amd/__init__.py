@@ -4,7 +4,8 @@ from packed low-bit codes, through the C ABI of libqlq (include/qlq.h).
 Group-wise affine n-bit weights (qlq_pack / qlq_linear_forward), ternary
 BitLinear (bitlinear_pack / bitlinear_forward) and per-channel W8A8
 (w8a8_linear_forward) with its per-group variant (pergroup_linear_forward),
-plus bit-exact helpers.  All computation runs in HIP
+per-column int4 weights with int8 activations (w4a8_linear_forward), plus
+bit-exact helpers.  All computation runs in HIP
 kernels; this package only marshals torch tensors into the C ABI.
 """
 
@@ -19,5 +20,6 @@ from .binding import (  # noqa: F401
     bitlinear_pack, bitlinear_forward,
     qlq_quantize_rows_int8, qlq_int8_matmul_int32, w8a8_workspace_size, w8a8_linear_forward,
     qlq_quantize_groups_int8, pergroup_workspace_size, pergroup_linear_forward,
+    w4a8_pack_weight_int4, w4a8_workspace_size, w4a8_linear_forward,
     qlq_device_check, qlq_version,
 )

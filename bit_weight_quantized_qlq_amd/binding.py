@@ -56,6 +56,9 @@ SIGNATURES = {
     "qlq_quantize_groups_int8": (_int, [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp]),
     "pergroup_workspace_size": (_sz, [_i64, _i64]),
     "pergroup_linear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _int, _vp, _vp, _vp, _sz, _vp]),
+    "w4a8_pack_weight_int4": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp]),
+    "w4a8_workspace_size": (_sz, [_i64, _i64]),
+    "w4a8_linear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "qlq_device_check": (_int, [_int]),
     "qlq_last_error": (ctypes.c_char_p, []),
     "qlq_version": (ctypes.c_char_p, []),
@@ -303,6 +306,46 @@ def pergroup_linear_forward(x, w, scale_w, group_size, bias=None, out=None, work
     _check(lib().pergroup_linear_forward(_ptr(x2), DTYPE_CODE[x.dtype], M, K, _ptr(w), _ptr(scale_w), N,
                                          group_size, _ptr(bias), _ptr(out), _ptr(workspace), ws_bytes,
                                          _stream(x)))
+    return out.reshape(*x.shape[:-1], N)
+
+
+# ------------------------------------------------ per-column int4, W4A8
+def w4a8_pack_weight_int4(w):
+    """Per-column symmetric int4: w [K, N] -> (packed uint8 [K/2, N], scale f32 [N])."""
+    _dev(w, "w", tuple(DTYPE_CODE), 2)
+    K, N = w.shape
+    packed = torch.empty((K // 2, N), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _check(lib().w4a8_pack_weight_int4(_ptr(w), DTYPE_CODE[w.dtype], K, N, _ptr(packed), _ptr(s), _stream(w)))
+    return packed, s
+
+
+def w4a8_workspace_size(M, K):
+    return int(lib().w4a8_workspace_size(M, K))
+
+
+def w4a8_linear_forward(x, packed_w, scale_w, bias=None, out=None, workspace=None):
+    """W4A8 linear: x [..., K] f16/bf16, packed_w uint8 [K/2, N], scale_w f32 [N]."""
+    _dev(x, "x", (torch.float16, torch.bfloat16))
+    _dev(packed_w, "packed_w", torch.uint8, 2)
+    _dev(scale_w, "scale_w", torch.float32, 1)
+    if bias is not None:
+        _dev(bias, "bias", x.dtype, 1)
+    x2 = _flatten(x)
+    M, K = x2.shape
+    N = packed_w.shape[1]
+    if packed_w.shape[0] * 2 != K:
+        raise ValueError("packed_w must be [K/2, N]")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _dev(out, "out", x.dtype)
+    need = w4a8_workspace_size(M, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().w4a8_linear_forward(_ptr(x2), DTYPE_CODE[x.dtype], M, K, _ptr(packed_w), _ptr(scale_w), N,
+                                     _ptr(bias), _ptr(out), _ptr(workspace), ws_bytes, _stream(x)))
     return out.reshape(*x.shape[:-1], N)
 
 

@@ -381,4 +381,47 @@ QLQ_API int pergroup_linear_forward(const void* x, int x_dtype, int64_t M, int64
                     "per-group int8 gemm");
 }
 
+QLQ_API int w4a8_pack_weight_int4(const void* w, int w_dtype, int64_t K, int64_t N, uint8_t* packed, float* scale,
+                                  void* stream) {
+  QLQ_REQUIRE(w && packed && scale, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(K >= 2 && K < kMaxDim && N >= 0 && N < kMaxDim, QLQ_ERR_INVALID_ARG, "invalid shape");
+  QLQ_REQUIRE(K % 2 == 0, QLQ_ERR_INVALID_ARG, "K=%lld is odd", (long long)K);
+  QLQ_REQUIRE(dtype_ok(w_dtype), QLQ_ERR_UNSUPPORTED, "w_dtype %d", w_dtype);
+  QLQ_REQUIRE(aligned(w, dtype_size(w_dtype)) && aligned(scale, 4), QLQ_ERR_ALIGNMENT, "misaligned pointer");
+  if (N == 0) return ok();
+  if (int st = current_device_status()) return st;
+  return hip_status(qlq::launch_pack_int4_cols(w, w_dtype, K, N, packed, scale, (hipStream_t)stream),
+                    "pack int4");
+}
+
+QLQ_API size_t w4a8_workspace_size(int64_t M, int64_t K) { return w8a8_workspace_size(M, K); }
+
+QLQ_API int w4a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed_w,
+                                const float* scale_w, int64_t N, const void* bias, void* y, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  QLQ_REQUIRE(x && packed_w && scale_w && y, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(M >= 0 && M < kMaxDim && N >= 1 && N < kMaxDim && K >= 16, QLQ_ERR_INVALID_ARG, "invalid shape");
+  QLQ_REQUIRE(K % 16 == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
+  QLQ_REQUIRE(K <= 131071, QLQ_ERR_UNSUPPORTED, "K=%lld could overflow int32", (long long)K);
+  QLQ_REQUIRE((K / 2) * N < kMaxDim, QLQ_ERR_UNSUPPORTED, "packed weight of %lld bytes above 2^31",
+              (long long)((K / 2) * N));
+  QLQ_REQUIRE(x_dtype == QLQ_F16 || x_dtype == QLQ_BF16, QLQ_ERR_UNSUPPORTED, "x_dtype must be F16 or BF16");
+  QLQ_REQUIRE(aligned(x, 16) && aligned(packed_w, 4) && aligned(scale_w, 4) && aligned(y, 2) &&
+                  (!bias || aligned(bias, 2)),
+              QLQ_ERR_ALIGNMENT, "misaligned pointer");
+  QLQ_REQUIRE((M + 127) / 128 <= 65535, QLQ_ERR_UNSUPPORTED, "M too large for one launch");
+  if (M == 0) return ok();
+  const size_t need = w4a8_workspace_size(M, K);
+  QLQ_REQUIRE(workspace && workspace_bytes >= need, QLQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+              need, workspace ? workspace_bytes : (size_t)0);
+  QLQ_REQUIRE(aligned(workspace, 16), QLQ_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+  if (int st = current_device_status()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  int8_t* xq = (int8_t*)workspace;
+  float* sx = (float*)((char*)workspace + (((size_t)M * (size_t)K + 255) & ~(size_t)255));
+  if (int st = hip_status(qlq::launch_quantize_rows_int8(x, x_dtype, M, K, xq, sx, s, true), "activation quant"))
+    return st;
+  return hip_status(qlq::launch_w4a8_gemm(xq, packed_w, M, N, K, sx, scale_w, bias, x_dtype, y, s), "w4a8 gemm");
+}
+
 }  // extern "C"

@@ -57,6 +57,86 @@ __device__ __forceinline__ i32x16_v mma_i8(u32x4_v a, u32x4_v b, i32x16_v c) {
                                                 c, 0, 0, 0);
 }
 
+// ---- packed int4 B operand ([K/2, N] bytes, N contiguous; byte (kp, n) holds
+// k = 2 kp in its high nibble and k = 2 kp + 1 in its low nibble, value =
+// code - 8).  The MFMA wants 16 consecutive k of one column per lane, so the
+// tile is turned around on its way to LDS: each thread loads k-pair rows
+// 8 rg .. 8 rg + 7 of columns 4 cg .. 4 cg + 3 (one dword per row), transposes
+// the two 4x4 byte blocks with byte permutes, and writes per column one
+// 16-byte chunk of int8 values 16 (code - 8): high nibbles (code << 4) ^ 0x80,
+// low nibbles ((code << 4) & 0xF0) ^ 0x80, i.e. chunk order k = 0 2 4 6 1 3 5 7
+// 8 10 12 14 9 11 13 15 (the activations are stored in the same order).  The
+// factor 16 comes off the int32 sum exactly (>> 4).
+namespace w4 {
+// slot of chunk c in B row r: the 8-lane groups that write rows 4 cg + j
+// (cg = 8a .. 8a+7) and the fragment reads of 8 or 16 consecutive rows both
+// meet distinct slots
+__device__ __forceinline__ int swz(int r) { return (r & 15) ^ ((r >> 4) & 1); }
+
+// o[c] = bytes c of r0..r3 (column c of a 4-row block)
+__device__ __forceinline__ void transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, uint32_t (&o)[4]) {
+  const uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
+  const uint32_t t1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
+  const uint32_t t2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// this thread's 8 packed rows of the tile starting at k-pair kp0.  Every
+// address stays inside the matrix: columns past N repeat the last in-range
+// column group (their outputs are never stored) and, on the last tile, rows
+// past K/2 repeat the last row (their activations are zero).  BYTES: N not a
+// multiple of 4, one byte per load.
+template <bool BYTES>
+__device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int kp0, int K2, int N, int ncols, int rg, int cg,
+                                     uint32_t (&bw)[8]) {
+  if constexpr (!BYTES) {
+    const int col = min(4 * cg, ncols - 4);
+    if (kp0 + 128 <= K2) {
+      const int vo = 8 * rg * N + col;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, vo, (kp0 + i) * N, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        bw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, min(kp0 + 8 * rg + i, K2 - 1) * N + col, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ro = min(kp0 + 8 * rg + i, K2 - 1) * N;
+      uint32_t v = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, ro + min(4 * cg + j, ncols - 1), 0, 0) << (8 * j);
+      bw[i] = v;
+    }
+  }
+}
+
+// unpack and write this thread's four 16-byte chunks into the B tile (rows of
+// BK bytes)
+template <int BK>
+__device__ __forceinline__ void store(int8_t* tile, const uint32_t (&bw)[8], int rg, int cg) {
+  uint32_t lo[4], hi[4];
+  transpose4(bw[0], bw[1], bw[2], bw[3], lo);
+  transpose4(bw[4], bw[5], bw[6], bw[7], hi);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int row = 4 * cg + c;
+    u32x4_v v;
+    v[0] = (lo[c] & 0xF0F0F0F0u) ^ 0x80808080u;
+    v[1] = ((lo[c] << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
+    v[2] = (hi[c] & 0xF0F0F0F0u) ^ 0x80808080u;
+    v[3] = ((hi[c] << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
+    *reinterpret_cast<u32x4_v*>(tile + row * BK + ((rg ^ swz(row)) << 4)) = v;
+  }
+}
+}  // namespace w4
+
 // Pipeline (one barrier per k-iteration).  Before iteration `it`, tiles
 // it .. it+STAGES-2 are in flight to their ring slots.  Iteration it: wait
 // until this thread's loads of tile it have landed, barrier (every thread's
@@ -70,14 +150,21 @@ __device__ __forceinline__ i32x16_v mma_i8(u32x4_v a, u32x4_v b, i32x16_v c) {
 // than a wave's half of an iteration is flushed once per half: the scale is
 // the same, the sum is linear), and y = acc_f * sa[m] (+ bias).  The int32
 // partial of one flush is below 2^24, so its conversion is exact.
-template <int OUT, int BK, int STAGES, int PG = 0>
+//
+// BSRC != 0: b is packed int4 [K/2, N] (namespace w4), loaded into registers
+// one tile ahead and written to the B half of the ring slot after the MFMAs
+// of the current tile (BSRC 2: byte loads, for N % 4 != 0).
+template <int OUT, int BK, int STAGES, int PG = 0, int BSRC = 0>
 __global__ void __launch_bounds__(i8::THREADS, 1)
-int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int M, int N, int K,
+int8_gemm_kernel(const int8_t* __restrict__ a, const void* __restrict__ b, int M, int N, int K,
                  const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
                  void* __restrict__ out) {
   using namespace i8;
   using C = Cfg<BK, STAGES>;
+  constexpr bool W4 = BSRC != 0;
   static_assert(PG == 0 || (OUT != 0 && PG % KS == 0), "per-group scales need a scaled output");
+  static_assert(!W4 || (PG == 0 && OUT != 0 && BK == 256 && STAGES == 2 && THREADS == 512),
+                "int4 B: 128 k-pair rows x 128 columns, 32 bytes per thread, double buffer");
   constexpr int FS = PG == 0 ? C::QN : (PG / KS < C::QN ? PG / KS : C::QN);  // k-steps per flush
   constexpr int NF = C::QN / FS;                                              // flushes per k-iteration
   // the ring during the K loop, then the 64 KiB of int32 partial sums that
@@ -95,7 +182,11 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
 
   const int rows_a = min(BM, M - m_blk), rows_b = min(BN, N - n_blk);
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(a + (int64_t)m_blk * K, rows_a * K);
-  const __amdgpu_buffer_rsrc_t rsb = make_rsrc(b + (int64_t)n_blk * K, rows_b * K);
+  const int K2 = K / 2;
+  const __amdgpu_buffer_rsrc_t rsb =
+      W4 ? make_rsrc((const uint8_t*)b + n_blk, K2 * N - n_blk)
+         : make_rsrc((const int8_t*)b + (int64_t)n_blk * K, rows_b * K);
+  const int cg = tid & 31, rg = tid >> 5;  // int4 B: column group, k-pair row group
   // load j of this thread: row wid*ROWS_W + RPI*j + lane/CPR of both tiles,
   // chunk (lane % CPR) ^ swz(row), i.e. LDS slot lane % CPR
   int voff[C::LPW], kc[C::LPW];
@@ -112,7 +203,7 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
     _Pragma("unroll") for (int j = 0; j < C::LPW; ++j) {                                        \
       const int o_ = k0_ + kc[j] < K ? voff[j] + k0_ : kOutOfRange;                             \
       load_lds_b128(rsa, dst_ + 1024 * j, o_);                                                  \
-      load_lds_b128(rsb, dst_ + C::TILE + 1024 * j, o_);                                        \
+      if constexpr (!W4) load_lds_b128(rsb, dst_ + C::TILE + 1024 * j, o_);                     \
     }                                                                                           \
   } while (0)
 
@@ -125,7 +216,7 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
     for (int i = 0; i < 2; ++i) {
       const int ra = wm * 64 + 32 * i + (lane & 31), rb = wn * 64 + 32 * i + (lane & 31);
       aoff[i][q] = ra * BK + (c ^ C::swz(ra)) * 16;
-      boff[i][q] = C::TILE + rb * BK + (c ^ C::swz(rb)) * 16;
+      boff[i][q] = C::TILE + rb * BK + (c ^ (W4 ? w4::swz(rb) : C::swz(rb))) * 16;
     }
   }
 
@@ -143,8 +234,11 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
   for (int j = 0; j < 2; ++j) ncol[j] = min(n_blk + wn * 64 + 32 * j + (lane & 31), N - 1);
   const int ng = PG ? K / (PG ? PG : 1) : 1;
 
+  uint32_t bw[8];  // int4 B: the next tile's packed rows
+  if constexpr (W4) w4::load<BSRC == 2>(rsb, 0, K2, N, N - n_blk, rg, cg, bw);
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t) QLQ_ISSUE(t);
+  if constexpr (W4) w4::store<BK>(smem + C::TILE, bw, rg, cg);
   for (int it = 0; it < nk; ++it) {
     // this thread's loads of tile it are done when at most the later
     // STAGES-2 tiles' loads are outstanding; then the barrier
@@ -160,6 +254,9 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
         for (int j = 0; j < 2; ++j) scf[f][j] = sb[(int64_t)g * N + ncol[j]];
       }
     }
+    const bool more = W4 && it + 1 < nk;
+    if constexpr (W4)
+      if (more) w4::load<BSRC == 2>(rsb, (it + 1) * (BK / 2), K2, N, N - n_blk, rg, cg, bw);
     QLQ_ISSUE(it + STAGES - 1);
     const int8_t* st_ = smem + (it % STAGES) * C::STAGE;
     u32x4_v af[2][C::QN], bf[2][C::QN];
@@ -190,6 +287,8 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
         }
       }
     }
+    if constexpr (W4)
+      if (more) w4::store<BK>(smem + ((it + 1) % STAGES) * C::STAGE + C::TILE, bw, rg, cg);
   }
 #undef QLQ_ISSUE
   // the zero tiles issued past the end may still be landing in the ring
@@ -269,7 +368,7 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const int8_t* __restrict__ b, int
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          if constexpr (PG == 0) v[i][j][e] = ((float)acc[i][j][e] * sam[i][e]) * sbn[j];
+          if constexpr (PG == 0) v[i][j][e] = ((float)(W4 ? acc[i][j][e] >> 4 : acc[i][j][e]) * sam[i][e]) * sbn[j];
           else v[i][j][e] = accf[i][j][e] * sam[i][e];
           if (bias) v[i][j][e] = v[i][j][e] + bn[j];
         }
@@ -316,6 +415,24 @@ hipError_t launch_int8_gemm_pergroup(const int8_t* a, const int8_t* b, int64_t M
     default: if (h) QLQ_PG_LAUNCH(1, 256); else QLQ_PG_LAUNCH(2, 256); break;
   }
 #undef QLQ_PG_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_gemm(const int8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                            const float* sa, const float* sb, const void* bias, int out_dtype, void* out,
+                            hipStream_t s) {
+  const int64_t tiles = cdiv(M, i8::BM) * cdiv(N, i8::BN);
+  dim3 grid((unsigned)tiles), block(i8::THREADS);
+  const int m = (int)M, n = (int)N, k = (int)K;
+#define QLQ_W4_LAUNCH(OUTV, SRC) \
+  hipLaunchKernelGGL((int8_gemm_kernel<OUTV, 256, 2, 0, SRC>), grid, block, 0, s, a, b, m, n, k, sa, sb, bias, out)
+  const bool h = out_dtype == F16;
+  if (N % 4 == 0) {
+    if (h) QLQ_W4_LAUNCH(1, 1); else QLQ_W4_LAUNCH(2, 1);
+  } else {
+    if (h) QLQ_W4_LAUNCH(1, 2); else QLQ_W4_LAUNCH(2, 2);
+  }
+#undef QLQ_W4_LAUNCH
   return hipGetLastError();
 }
 

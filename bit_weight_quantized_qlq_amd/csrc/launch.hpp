@@ -19,8 +19,12 @@ hipError_t launch_affine_dequant(const uint32_t* packed, const void* scales, con
                                  hipStream_t s);
 hipError_t launch_ternary_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* packed,
                                int* err_flag, hipStream_t s);
+// nibble_order: each 16-byte chunk of q in the order eight packed int4 bytes
+// unpack to (high nibbles then low nibbles, four bytes at a time)
 hipError_t launch_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_t K,
-                                     int8_t* q, float* scale, hipStream_t s);
+                                     int8_t* q, float* scale, hipStream_t s, bool nibble_order = false);
+hipError_t launch_pack_int4_cols(const void* w, int w_dtype, int64_t K, int64_t N, uint8_t* packed,
+                                 float* scale, hipStream_t s);
 
 // gemv.hip: skinny affine forward (small M)
 hipError_t launch_affine_gemv(const void* x, int x_dtype, int64_t M, int64_t K,
@@ -44,6 +48,11 @@ hipError_t launch_ternary_forward(const void* x, int x_dtype, int64_t M, int64_t
 hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K,
                             const float* sa, const float* sb, const void* bias, int out_dtype,
                             void* out, hipStream_t s);
+// b: packed int4 [K/2, N] (even k in the high nibble, value = code - 8);
+// a: int8 [M, K] in nibble order; y = fp32(a . b) * sa[m] * sb[n] (+ bias)
+hipError_t launch_w4a8_gemm(const int8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
+                            const float* sa, const float* sb, const void* bias, int out_dtype, void* out,
+                            hipStream_t s);
 hipError_t launch_int8_gemm_pergroup(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K,
                                      const float* sa, const float* scale_w, int group_size,
                                      const void* bias, int out_dtype, void* out, hipStream_t s);

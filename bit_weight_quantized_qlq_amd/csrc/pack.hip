@@ -227,7 +227,18 @@ struct RowDivider {
   }
 };
 
-template <typename T>
+// Output order inside each 16-byte chunk.  NIB = false: k order.  NIB = true:
+// the order in which a chunk's sixteen values come out of eight packed int4
+// bytes split into high then low nibbles, four bytes at a time: slot s holds
+// element (s & 8) | ((s & 3) << 1) | ((s >> 2) & 1), i.e. k = 0 2 4 6 1 3 5 7
+// 8 10 12 14 9 11 13 15.  A dot product over a chunk is the same sum either
+// way when both operands use one order.
+template <bool NIB>
+__host__ __device__ constexpr int chunk_src(int s) {
+  return NIB ? ((s & 8) | ((s & 3) << 1) | ((s >> 2) & 1)) : s;
+}
+
+template <typename T, bool NIB>
 __global__ void __launch_bounds__(256)
 quantize_rows_int8_kernel(const T* __restrict__ v, int64_t K, int8_t* __restrict__ q,
                           float* __restrict__ scale) {
@@ -262,7 +273,7 @@ quantize_rows_int8_kernel(const T* __restrict__ v, int64_t K, int8_t* __restrict
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float r = rintf(dv.div(e[4 * i + j]));
+        float r = rintf(dv.div(e[chunk_src<NIB>(4 * i + j)]));
         r = fminf(fmaxf(r, -128.0f), 127.0f);
         word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
       }
@@ -275,7 +286,7 @@ quantize_rows_int8_kernel(const T* __restrict__ v, int64_t K, int8_t* __restrict
 // Register-resident variant for K <= 64 * EPT: one wave per row, each lane
 // keeps its EPT consecutive elements (16-byte loads) in registers, so the row
 // is read once; max by DPP; no block barrier.
-template <typename T, int EPT>
+template <typename T, int EPT, bool NIB>
 __global__ void __launch_bounds__(256)
 quantize_rows_int8_wave_kernel(const T* __restrict__ v, int R, int K, int8_t* __restrict__ q,
                                float* __restrict__ scale) {
@@ -312,7 +323,7 @@ quantize_rows_int8_wave_kernel(const T* __restrict__ v, int R, int K, int8_t* __
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float r = rintf(dv.div(e[g * 16 + 4 * i + j]));
+        float r = rintf(dv.div(e[g * 16 + chunk_src<NIB>(4 * i + j)]));
         r = fminf(fmaxf(r, -128.0f), 127.0f);
         word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
       }
@@ -325,7 +336,7 @@ quantize_rows_int8_wave_kernel(const T* __restrict__ v, int R, int K, int8_t* __
 // One 256-thread block per row, EPT elements per thread (16-element groups
 // interleaved across the block: coalesced 16-byte loads and stores); the row
 // stays in registers between the max and the quantization.
-template <typename T, int EPT>
+template <typename T, int EPT, bool NIB>
 __global__ void __launch_bounds__(256)
 quantize_rows_int8_block_kernel(const T* __restrict__ v, int K, int8_t* __restrict__ q,
                                 float* __restrict__ scale) {
@@ -365,7 +376,7 @@ quantize_rows_int8_block_kernel(const T* __restrict__ v, int K, int8_t* __restri
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float r = rintf(dv.div(e[g * 16 + 4 * i + j]));
+        float r = rintf(dv.div(e[g * 16 + chunk_src<NIB>(4 * i + j)]));
         r = fminf(fmaxf(r, -128.0f), 127.0f);
         word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
       }
@@ -442,33 +453,94 @@ hipError_t launch_quantize_groups_int8(const void* w, int w_dtype, int64_t N, in
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool NIB>
 static void quant_rows_launch(const void* v, int64_t R, int64_t K, int8_t* q, float* scale, hipStream_t s) {
   // short rows: a wave per row; up to 16384: a block per row (four times the
   // waves, so the per-element work spreads over every SIMD); longer: two
   // passes over the row
   if (K <= 64 * 16) {
-    hipLaunchKernelGGL((quantize_rows_int8_wave_kernel<T, 16>), dim3((unsigned)cdiv(R, 4)), dim3(256), 0, s,
+    hipLaunchKernelGGL((quantize_rows_int8_wave_kernel<T, 16, NIB>), dim3((unsigned)cdiv(R, 4)), dim3(256), 0, s,
                        (const T*)v, (int)R, (int)K, q, scale);
   } else if (K <= 256 * 64) {
     dim3 grid((unsigned)R), block(256);
     if (K <= 256 * 16)
-      hipLaunchKernelGGL((quantize_rows_int8_block_kernel<T, 16>), grid, block, 0, s, (const T*)v, (int)K, q, scale);
+      hipLaunchKernelGGL((quantize_rows_int8_block_kernel<T, 16, NIB>), grid, block, 0, s, (const T*)v, (int)K, q,
+                         scale);
     else if (K <= 256 * 32)
-      hipLaunchKernelGGL((quantize_rows_int8_block_kernel<T, 32>), grid, block, 0, s, (const T*)v, (int)K, q, scale);
+      hipLaunchKernelGGL((quantize_rows_int8_block_kernel<T, 32, NIB>), grid, block, 0, s, (const T*)v, (int)K, q,
+                         scale);
     else
-      hipLaunchKernelGGL((quantize_rows_int8_block_kernel<T, 64>), grid, block, 0, s, (const T*)v, (int)K, q, scale);
+      hipLaunchKernelGGL((quantize_rows_int8_block_kernel<T, 64, NIB>), grid, block, 0, s, (const T*)v, (int)K, q,
+                         scale);
   } else {
-    hipLaunchKernelGGL(quantize_rows_int8_kernel<T>, dim3((unsigned)R), dim3(256), 0, s, (const T*)v, K, q, scale);
+    hipLaunchKernelGGL((quantize_rows_int8_kernel<T, NIB>), dim3((unsigned)R), dim3(256), 0, s, (const T*)v, K, q,
+                       scale);
   }
 }
 
 hipError_t launch_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_t K, int8_t* q,
-                                     float* scale, hipStream_t s) {
+                                     float* scale, hipStream_t s, bool nibble_order) {
+#define QLQ_QR(T) nibble_order ? quant_rows_launch<T, true>(v, R, K, q, scale, s) \
+                               : quant_rows_launch<T, false>(v, R, K, q, scale, s)
   switch (v_dtype) {
-    case F32: quant_rows_launch<float>(v, R, K, q, scale, s); break;
-    case BF16: quant_rows_launch<bf16_t>(v, R, K, q, scale, s); break;
-    default: quant_rows_launch<f16_t>(v, R, K, q, scale, s); break;
+    case F32: QLQ_QR(float); break;
+    case BF16: QLQ_QR(bf16_t); break;
+    default: QLQ_QR(f16_t); break;
+  }
+#undef QLQ_QR
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ per-column int4 packing
+// w [K, N] (row-major, N contiguous) -> packed [K/2, N] uint8 with the even k
+// in the high nibble, and scale [N] fp32: s = absmax of the column / 7 (1 if
+// 0), code = clamp(rint(w / s) + 8, 0, 15), the quotient correctly rounded.
+// A block covers 64 consecutive columns (a wave reads 64 neighbours of one
+// row) with its four waves splitting the rows: pass 1 takes each wave's
+// column maxima over rows k = wave, wave + 4, ..., LDS joins the four; pass 2
+// writes k-pair rows kp = wave, wave + 4, ...
+template <typename T>
+__global__ void __launch_bounds__(256)
+pack_int4_cols_kernel(const T* __restrict__ w, int K, int N, uint8_t* __restrict__ packed,
+                      float* __restrict__ scale) {
+  __shared__ float red[4][64];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int n = blockIdx.x * 64 + tx;
+  const bool in = n < N;
+  float a = 0.0f;
+  if (in)
+    for (int k = ty; k < K; k += 4) a = fmaxf(a, fabsf(Elem<T>::load(w, (int64_t)k * N + n)));
+  red[ty][tx] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0][tx], red[1][tx]), fmaxf(red[2][tx], red[3][tx]));
+  float sc = __fdiv_rn(a, 7.0f);
+  if (sc == 0.0f) sc = 1.0f;
+  if (!in) return;
+  if (ty == 0) scale[n] = sc;
+  const RowDivider dv(sc);
+  for (int kp = ty; kp < K / 2; kp += 4) {
+    const float h = fminf(fmaxf(rintf(dv.div(Elem<T>::load(w, (int64_t)(2 * kp) * N + n))) + 8.0f, 0.0f), 15.0f);
+    const float l = fminf(fmaxf(rintf(dv.div(Elem<T>::load(w, (int64_t)(2 * kp + 1) * N + n))) + 8.0f, 0.0f), 15.0f);
+    packed[(int64_t)kp * N + n] = (uint8_t)(((int)h << 4) | (int)l);
+  }
+}
+
+hipError_t launch_pack_int4_cols(const void* w, int w_dtype, int64_t K, int64_t N, uint8_t* packed, float* scale,
+                                 hipStream_t s) {
+  const dim3 grid((unsigned)cdiv(N, 64)), block(256);
+  switch (w_dtype) {
+    case F32:
+      hipLaunchKernelGGL(pack_int4_cols_kernel<float>, grid, block, 0, s, (const float*)w, (int)K, (int)N, packed,
+                         scale);
+      break;
+    case BF16:
+      hipLaunchKernelGGL(pack_int4_cols_kernel<bf16_t>, grid, block, 0, s, (const bf16_t*)w, (int)K, (int)N,
+                         packed, scale);
+      break;
+    default:
+      hipLaunchKernelGGL(pack_int4_cols_kernel<f16_t>, grid, block, 0, s, (const f16_t*)w, (int)K, (int)N, packed,
+                         scale);
+      break;
   }
   return hipGetLastError();
 }

@@ -268,6 +268,44 @@ QLQ_API int pergroup_linear_forward(const void* x, int x_dtype, int64_t M, int64
                                     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Per-column int4 weights, int8 activations ("cider/ops.py":
+ * pack_weight_int4, w4a8_linear)
+ * ------------------------------------------------------------------------ */
+
+/*
+ * w4a8_pack_weight_int4 - per-column symmetric int4 quantization of
+ * w [K, N] (row-major, N contiguous; w_dtype F32, F16 or BF16):
+ * s = max |w[:, n]| / 7 in fp32 (1 if 0), code = clamp(rint(w/s) + 8, 0, 15)
+ * with the quotient correctly rounded.  packed [K/2, N] uint8 (out): byte
+ * (j, n) holds the code of k = 2j in its high nibble and of k = 2j + 1 in its
+ * low nibble; scale [N] fp32 (out).  K even.  Non-finite weights give
+ * unspecified codes (no check on the device).
+ */
+QLQ_API int w4a8_pack_weight_int4(const void* w, int w_dtype, int64_t K, int64_t N,
+                                  uint8_t* packed, float* scale, void* stream);
+
+/* Bytes of workspace w4a8_linear_forward needs (as w8a8_workspace_size). */
+QLQ_API size_t w4a8_workspace_size(int64_t M, int64_t K);
+
+/*
+ * w4a8_linear_forward - y = dequant(quant_a(x) . unpack4(packed_w)) (+ bias)
+ * (w4a8_linear).  unpack4 gives the value code - 8 of each nibble; quant_a
+ * is per-row symmetric int8 as in qlq_quantize_rows_int8; the exact int32
+ * sum is scaled as acc * sx[m] * scale_w[n] (+ bias[n]) in fp32 and rounded
+ * once to x_dtype.  The pages' function has no bias: pass NULL for it.
+ *
+ *   x [M, K] of x_dtype (F16 or BF16); packed_w [K/2, N] uint8 as written by
+ *   w4a8_pack_weight_int4 (4-byte aligned); scale_w [N] fp32; bias [N] of
+ *   x_dtype or NULL; y [M, N] of x_dtype (out); workspace >=
+ *   w4a8_workspace_size(M, K) bytes, 16-byte aligned (overwritten, no state
+ *   kept between calls).  K % 16 == 0, K <= 131071, (K/2)*N < 2^31.
+ */
+QLQ_API int w4a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
+                                const uint8_t* packed_w, const float* scale_w, int64_t N,
+                                const void* bias, void* y, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Device and error reporting
  * ------------------------------------------------------------------------ */
 

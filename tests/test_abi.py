@@ -197,3 +197,42 @@ def test_pergroup_workspace_sizes():
     L = qlq.lib()
     assert L.pergroup_workspace_size(1, 4096) == 0
     assert L.pergroup_workspace_size(2, 4096) == L.w8a8_workspace_size(2, 4096) > 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, qlq.QLQ_F32, 64, 32, A, B, None), qlq.QLQ_ERR_INVALID_ARG),
+    ((A, qlq.QLQ_F32, 63, 32, A, B, None), qlq.QLQ_ERR_INVALID_ARG),      # K odd
+    ((A, qlq.QLQ_F32, 0, 32, A, B, None), qlq.QLQ_ERR_INVALID_ARG),
+    ((A, 9, 64, 32, A, B, None), qlq.QLQ_ERR_UNSUPPORTED),
+    ((ODD, qlq.QLQ_F32, 64, 32, A, B, None), qlq.QLQ_ERR_ALIGNMENT),
+    ((A, qlq.QLQ_F32, 64, 32, A, ODD, None), qlq.QLQ_ERR_ALIGNMENT),       # scale
+])
+def test_w4a8_pack_validation(args, code):
+    assert qlq.lib().w4a8_pack_weight_int4(*args) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=None), qlq.QLQ_ERR_INVALID_ARG),
+    (dict(K=40), qlq.QLQ_ERR_INVALID_ARG),                     # K % 16
+    (dict(K=131072), qlq.QLQ_ERR_UNSUPPORTED),                 # int32 headroom
+    (dict(K=65536, N=65536), qlq.QLQ_ERR_UNSUPPORTED),         # packed bytes >= 2^31
+    (dict(x_dtype=qlq.QLQ_F32), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(ws=None), qlq.QLQ_ERR_WORKSPACE),
+    (dict(ws_bytes=100), qlq.QLQ_ERR_WORKSPACE),
+    (dict(x=ODD), qlq.QLQ_ERR_ALIGNMENT),
+    (dict(w=ODD), qlq.QLQ_ERR_ALIGNMENT),                      # packed_w needs 4 bytes
+    (dict(ws=A + 8), qlq.QLQ_ERR_ALIGNMENT),
+])
+def test_w4a8_forward_validation(kw, code):
+    a = dict(x=A, x_dtype=qlq.QLQ_F16, M=16, K=64, w=B, sw=A, N=32, bias=None, y=A, ws=B, ws_bytes=1 << 20)
+    a.update(kw)
+    r = qlq.lib().w4a8_linear_forward(a["x"], a["x_dtype"], a["M"], a["K"], a["w"], a["sw"], a["N"],
+                                      a["bias"], a["y"], a["ws"], a["ws_bytes"], None)
+    assert r == code
+
+
+def test_w4a8_workspace_and_empty_batch():
+    L = qlq.lib()
+    assert L.w4a8_workspace_size(16, 4096) == L.w8a8_workspace_size(16, 4096) > 0
+    assert L.w4a8_workspace_size(0, 4096) == 0
+    assert L.w4a8_linear_forward(A, qlq.QLQ_F16, 0, 64, B, A, 32, None, A, None, 0, None) == 0
