@@ -57,7 +57,7 @@ SIGNATURES = {
     "pergroup_workspace_size": (_sz, [_i64, _i64]),
     "pergroup_linear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _int, _vp, _vp, _vp, _sz, _vp]),
     "w4a8_pack_weight_int4": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp]),
-    "w4a8_workspace_size": (_sz, [_i64, _i64]),
+    "w4a8_workspace_size": (_sz, [_i64, _i64, _i64]),
     "w4a8_linear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "qlq_device_check": (_int, [_int]),
     "qlq_last_error": (ctypes.c_char_p, []),
@@ -320,8 +320,8 @@ def w4a8_pack_weight_int4(w):
     return packed, s
 
 
-def w4a8_workspace_size(M, K):
-    return int(lib().w4a8_workspace_size(M, K))
+def w4a8_workspace_size(M, K, N):
+    return int(lib().w4a8_workspace_size(M, K, N))
 
 
 def w4a8_linear_forward(x, packed_w, scale_w, bias=None, out=None, workspace=None):
@@ -340,7 +340,7 @@ def w4a8_linear_forward(x, packed_w, scale_w, bias=None, out=None, workspace=Non
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     else:
         _dev(out, "out", x.dtype)
-    need = w4a8_workspace_size(M, K)
+    need = w4a8_workspace_size(M, K, N)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

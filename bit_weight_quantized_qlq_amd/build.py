@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqlq.so")
-SOURCES = ["api.cpp", "pack.hip", "gemv.hip", "gemm.hip", "ternary.hip", "int8.hip", "pergroup.hip"]
+SOURCES = ["api.cpp", "pack.hip", "gemv.hip", "gemm.hip", "ternary.hip", "int8.hip", "pergroup.hip", "w4a8.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -394,7 +394,13 @@ QLQ_API int w4a8_pack_weight_int4(const void* w, int w_dtype, int64_t K, int64_t
                     "pack int4");
 }
 
-QLQ_API size_t w4a8_workspace_size(int64_t M, int64_t K) { return w8a8_workspace_size(M, K); }
+QLQ_API size_t w4a8_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (M <= 0 || K <= 0 || N <= 0) return 0;
+  const size_t gemm = w8a8_workspace_size(M, K);
+  if (M > qlq::kW4a8SkinnyMaxM) return gemm;
+  const size_t skinny = qlq::w4a8_skinny_workspace(M, K, N);
+  return skinny > gemm ? skinny : gemm;
+}
 
 QLQ_API int w4a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed_w,
                                 const float* scale_w, int64_t N, const void* bias, void* y, void* workspace,
@@ -411,12 +417,15 @@ QLQ_API int w4a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K
               QLQ_ERR_ALIGNMENT, "misaligned pointer");
   QLQ_REQUIRE((M + 127) / 128 <= 65535, QLQ_ERR_UNSUPPORTED, "M too large for one launch");
   if (M == 0) return ok();
-  const size_t need = w4a8_workspace_size(M, K);
+  const size_t need = w4a8_workspace_size(M, K, N);
   QLQ_REQUIRE(workspace && workspace_bytes >= need, QLQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
               need, workspace ? workspace_bytes : (size_t)0);
   QLQ_REQUIRE(aligned(workspace, 16), QLQ_ERR_ALIGNMENT, "workspace not 16-byte aligned");
   if (int st = current_device_status()) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (M <= qlq::kW4a8SkinnyMaxM && M <= g_skinny_max_m)
+    return hip_status(qlq::launch_w4a8_skinny(x, x_dtype, M, K, packed_w, N, scale_w, bias, y, workspace, s),
+                      "w4a8 skinny");
   int8_t* xq = (int8_t*)workspace;
   float* sx = (float*)((char*)workspace + (((size_t)M * (size_t)K + 255) & ~(size_t)255));
   if (int st = hip_status(qlq::launch_quantize_rows_int8(x, x_dtype, M, K, xq, sx, s, true), "activation quant"))

@@ -219,4 +219,26 @@ __device__ __forceinline__ int lds_swz(int r) {
   else return r & 15;
 }
 
+// ---------------------------------------------- quotient by a row's scale
+// x / s rounded to nearest for one divisor s shared by a whole row: the
+// correctly rounded reciprocal y = RN(1/s) once, then per quotient q =
+// RN(x*y), the exact residual r = x - s*q (one fused multiply-add) and
+// RN(q + r*y), which is the correctly rounded quotient when y is the
+// correctly rounded reciprocal and nothing under- or overflows (Markstein's
+// correction step).  Here |x| <= 127 |s|; divisors outside [2^-100, 2^100]
+// keep the full division.
+struct RowDivider {
+  float s, y;
+  bool fast;
+  __device__ __forceinline__ explicit RowDivider(float s_) : s(s_), y(__fdiv_rn(1.0f, s_)) {
+    const float as = fabsf(s_);
+    fast = as >= 0x1p-100f && as <= 0x1p100f;
+  }
+  __device__ __forceinline__ float div(float x) const {
+    if (!fast) return __fdiv_rn(x, s);
+    const float q = x * y;
+    return fmaf(fmaf(-s, q, x), y, q);
+  }
+};
+
 }  // namespace qlq

@@ -22,6 +22,7 @@
 // c of row r at slot c ^ swz(r)), so the fragment reads of 8 or 16 lanes
 // (consecutive rows, same chunk) fall on distinct banks.
 #include "common.hpp"
+#include "int4.hpp"
 #include "launch.hpp"
 #include "tile.hpp"
 
@@ -57,64 +58,26 @@ __device__ __forceinline__ i32x16_v mma_i8(u32x4_v a, u32x4_v b, i32x16_v c) {
                                                 c, 0, 0, 0);
 }
 
-// ---- packed int4 B operand ([K/2, N] bytes, N contiguous; byte (kp, n) holds
-// k = 2 kp in its high nibble and k = 2 kp + 1 in its low nibble, value =
-// code - 8).  The MFMA wants 16 consecutive k of one column per lane, so the
-// tile is turned around on its way to LDS: each thread loads k-pair rows
-// 8 rg .. 8 rg + 7 of columns 4 cg .. 4 cg + 3 (one dword per row), transposes
-// the two 4x4 byte blocks with byte permutes, and writes per column one
-// 16-byte chunk of int8 values 16 (code - 8): high nibbles (code << 4) ^ 0x80,
-// low nibbles ((code << 4) & 0xF0) ^ 0x80, i.e. chunk order k = 0 2 4 6 1 3 5 7
-// 8 10 12 14 9 11 13 15 (the activations are stored in the same order).  The
-// factor 16 comes off the int32 sum exactly (>> 4).
+// ---- packed int4 B operand (BSRC != 0; layout and unpacking in int4.hpp).
+// The MFMA wants 16 consecutive k of one column per lane, so the tile is
+// turned around on its way to LDS: thread (rg, cg) loads k-pair rows
+// 8 rg .. 8 rg + 7 of columns 4 cg .. 4 cg + 3, and writes per column one
+// 16-byte chunk of int8 values 16 (code - 8), in the chunk order the
+// activations are stored in.  The factor 16 comes off the int32 sum exactly
+// (>> 4).
 namespace w4 {
 // slot of chunk c in B row r: the 8-lane groups that write rows 4 cg + j
 // (cg = 8a .. 8a+7) and the fragment reads of 8 or 16 consecutive rows both
 // meet distinct slots
 __device__ __forceinline__ int swz(int r) { return (r & 15) ^ ((r >> 4) & 1); }
 
-// o[c] = bytes c of r0..r3 (column c of a 4-row block)
-__device__ __forceinline__ void transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3, uint32_t (&o)[4]) {
-  const uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
-  const uint32_t t1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
-  const uint32_t t2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
-  const uint32_t t3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
-  o[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-  o[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-  o[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-  o[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
-}
-
-// this thread's 8 packed rows of the tile starting at k-pair kp0.  Every
-// address stays inside the matrix: columns past N repeat the last in-range
-// column group (their outputs are never stored) and, on the last tile, rows
-// past K/2 repeat the last row (their activations are zero).  BYTES: N not a
-// multiple of 4, one byte per load.
+// this thread's 8 packed rows of the 128-row tile starting at k-pair kp0;
+// columns past N repeat the last in-range column group (never stored)
 template <bool BYTES>
 __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int kp0, int K2, int N, int ncols, int rg, int cg,
                                      uint32_t (&bw)[8]) {
-  if constexpr (!BYTES) {
-    const int col = min(4 * cg, ncols - 4);
-    if (kp0 + 128 <= K2) {
-      const int vo = 8 * rg * N + col;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) bw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, vo, (kp0 + i) * N, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        bw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, min(kp0 + 8 * rg + i, K2 - 1) * N + col, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ro = min(kp0 + 8 * rg + i, K2 - 1) * N;
-      uint32_t v = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, ro + min(4 * cg + j, ncols - 1), 0, 0) << (8 * j);
-      bw[i] = v;
-    }
-  }
+  const int col = BYTES ? 4 * cg : min(4 * cg, ncols - 4);
+  int4::load8<BYTES>(r, kp0, 8 * rg, kp0 + 128 <= K2, K2, N, ncols, col, bw);
 }
 
 // unpack and write this thread's four 16-byte chunks into the B tile (rows of
@@ -122,17 +85,12 @@ __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int kp0, int K2, 
 template <int BK>
 __device__ __forceinline__ void store(int8_t* tile, const uint32_t (&bw)[8], int rg, int cg) {
   uint32_t lo[4], hi[4];
-  transpose4(bw[0], bw[1], bw[2], bw[3], lo);
-  transpose4(bw[4], bw[5], bw[6], bw[7], hi);
+  int4::transpose4(bw[0], bw[1], bw[2], bw[3], lo);
+  int4::transpose4(bw[4], bw[5], bw[6], bw[7], hi);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int row = 4 * cg + c;
-    u32x4_v v;
-    v[0] = (lo[c] & 0xF0F0F0F0u) ^ 0x80808080u;
-    v[1] = ((lo[c] << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
-    v[2] = (hi[c] & 0xF0F0F0F0u) ^ 0x80808080u;
-    v[3] = ((hi[c] << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
-    *reinterpret_cast<u32x4_v*>(tile + row * BK + ((rg ^ swz(row)) << 4)) = v;
+    *reinterpret_cast<u32x4_v*>(tile + row * BK + ((rg ^ swz(row)) << 4)) = int4::unpack16(lo[c], hi[c]);
   }
 }
 }  // namespace w4

@@ -53,6 +53,12 @@ hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, int64_t M, int64_t
 hipError_t launch_w4a8_gemm(const int8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
                             const float* sa, const float* sb, const void* bias, int out_dtype, void* out,
                             hipStream_t s);
+// w4a8.hip: a few rows (M <= kW4a8SkinnyMaxM), split over K; workspace of
+// w4a8_skinny_workspace bytes (int32 partials, then the row scales)
+constexpr int64_t kW4a8SkinnyMaxM = 8;
+size_t w4a8_skinny_workspace(int64_t M, int64_t K, int64_t N);
+hipError_t launch_w4a8_skinny(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* b, int64_t N,
+                              const float* sw, const void* bias, void* y, void* workspace, hipStream_t s);
 hipError_t launch_int8_gemm_pergroup(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K,
                                      const float* sa, const float* scale_w, int group_size,
                                      const void* bias, int out_dtype, void* out, hipStream_t s);

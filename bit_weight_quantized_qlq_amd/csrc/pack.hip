@@ -13,6 +13,7 @@
 // quantizes activations on the W8A8 forward path and is written for
 // bandwidth (one wave per row, the row held in registers).
 #include "common.hpp"
+#include "int4.hpp"
 #include "launch.hpp"
 
 namespace qlq {
@@ -206,36 +207,12 @@ hipError_t launch_ternary_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* p
 // One 256-thread block per row.  Pass 1: exact fp32 absmax (block reduction).
 // Pass 2: q = clamp(rint(v / s), -128, 127) with s = a / 127 (1 if 0).
 // Each thread handles 16 consecutive elements per step (K % 16 == 0).
-// x / s rounded to nearest for one divisor s shared by a whole row: the
-// correctly rounded reciprocal y = RN(1/s) once, then per quotient q =
-// RN(x*y), the exact residual r = x - s*q (one fused multiply-add) and
-// RN(q + r*y), which is the correctly rounded quotient when y is the
-// correctly rounded reciprocal and nothing under- or overflows (Markstein's
-// correction step).  Here |x| <= 127 |s|; divisors outside [2^-100, 2^100]
-// keep the full division.
-struct RowDivider {
-  float s, y;
-  bool fast;
-  __device__ __forceinline__ explicit RowDivider(float s_) : s(s_), y(__fdiv_rn(1.0f, s_)) {
-    const float as = fabsf(s_);
-    fast = as >= 0x1p-100f && as <= 0x1p100f;
-  }
-  __device__ __forceinline__ float div(float x) const {
-    if (!fast) return __fdiv_rn(x, s);
-    const float q = x * y;
-    return fmaf(fmaf(-s, q, x), y, q);
-  }
-};
 
-// Output order inside each 16-byte chunk.  NIB = false: k order.  NIB = true:
-// the order in which a chunk's sixteen values come out of eight packed int4
-// bytes split into high then low nibbles, four bytes at a time: slot s holds
-// element (s & 8) | ((s & 3) << 1) | ((s >> 2) & 1), i.e. k = 0 2 4 6 1 3 5 7
-// 8 10 12 14 9 11 13 15.  A dot product over a chunk is the same sum either
-// way when both operands use one order.
+// Output order inside each 16-byte chunk: k order, or (NIB) the order packed
+// int4 bytes unpack to (int4::act_slot).
 template <bool NIB>
 __host__ __device__ constexpr int chunk_src(int s) {
-  return NIB ? ((s & 8) | ((s & 3) << 1) | ((s >> 2) & 1)) : s;
+  return NIB ? int4::act_slot(s) : s;
 }
 
 template <typename T, bool NIB>

@@ -284,8 +284,10 @@ QLQ_API int pergroup_linear_forward(const void* x, int x_dtype, int64_t M, int64
 QLQ_API int w4a8_pack_weight_int4(const void* w, int w_dtype, int64_t K, int64_t N,
                                   uint8_t* packed, float* scale, void* stream);
 
-/* Bytes of workspace w4a8_linear_forward needs (as w8a8_workspace_size). */
-QLQ_API size_t w4a8_workspace_size(int64_t M, int64_t K);
+/* Bytes of workspace w4a8_linear_forward needs: quant_a(x) and its row
+ * scales for the GEMM; for M <= 8 at least the skinny path's exact int32
+ * partial sums (one per 128 input values, row and column) and row scales. */
+QLQ_API size_t w4a8_workspace_size(int64_t M, int64_t K, int64_t N);
 
 /*
  * w4a8_linear_forward - y = dequant(quant_a(x) . unpack4(packed_w)) (+ bias)
@@ -293,11 +295,14 @@ QLQ_API size_t w4a8_workspace_size(int64_t M, int64_t K);
  * is per-row symmetric int8 as in qlq_quantize_rows_int8; the exact int32
  * sum is scaled as acc * sx[m] * scale_w[n] (+ bias[n]) in fp32 and rounded
  * once to x_dtype.  The pages' function has no bias: pass NULL for it.
+ * M <= min(8, qlq_get_skinny_max_m()) takes a kernel split over K (exact
+ * int32 partials, then a kernel that adds them and scales); larger M the
+ * GEMM.  Both give identical outputs (the sums are exact integers).
  *
  *   x [M, K] of x_dtype (F16 or BF16); packed_w [K/2, N] uint8 as written by
  *   w4a8_pack_weight_int4 (4-byte aligned); scale_w [N] fp32; bias [N] of
  *   x_dtype or NULL; y [M, N] of x_dtype (out); workspace >=
- *   w4a8_workspace_size(M, K) bytes, 16-byte aligned (overwritten, no state
+ *   w4a8_workspace_size(M, K, N) bytes, 16-byte aligned (overwritten, no state
  *   kept between calls).  K % 16 == 0, K <= 131071, (K/2)*N < 2^31.
  */
 QLQ_API int w4a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,

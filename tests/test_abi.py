@@ -233,6 +233,9 @@ def test_w4a8_forward_validation(kw, code):
 
 def test_w4a8_workspace_and_empty_batch():
     L = qlq.lib()
-    assert L.w4a8_workspace_size(16, 4096) == L.w8a8_workspace_size(16, 4096) > 0
-    assert L.w4a8_workspace_size(0, 4096) == 0
+    assert L.w4a8_workspace_size(16, 4096, 4096) == L.w8a8_workspace_size(16, 4096) > 0
+    assert L.w4a8_workspace_size(0, 4096, 4096) == 0
+    # M <= 8: room for the split-K partials (32 splits of 128 input values)
+    assert L.w4a8_workspace_size(1, 4096, 4096) >= 32 * 4096 * 4 + 4
+    assert L.w4a8_workspace_size(8, 4096, 64) >= L.w8a8_workspace_size(8, 4096)
     assert L.w4a8_linear_forward(A, qlq.QLQ_F16, 0, 64, B, A, 32, None, A, None, 0, None) == 0

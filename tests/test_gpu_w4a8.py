@@ -106,3 +106,26 @@ def test_zero_input_gives_bias():
     bias = (torch.arange(N, device=dev(), dtype=torch.float32) / 8).to(torch.float16)
     y = qlq.w4a8_linear_forward(torch.zeros(5, K, device=dev(), dtype=torch.float16), packed, s, bias=bias)
     assert torch.equal(y, bias.expand(5, N))
+
+
+@pytest.mark.parametrize("xdt", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (2, 272, 132), (3, 1040, 517), (4, 128, 260),
+                                   (5, 2048, 384), (8, 16, 4), (7, 784, 1)])
+def test_skinny_and_gemm_paths_identical(xdt, M, K, N):
+    """M <= 8 runs split over K; the GEMM gives the same exact int32 sums and
+    the same epilogue, so the two outputs must be bit-identical."""
+    inp = workloads.w4a8_inputs(M, K, N, x_dtype=ODT[xdt], bias=True, seed=M + K + N, outlier_frac=0.01)
+    packed, s = qlq.w4a8_pack_weight_int4(inp["w"].to(dev()))
+    x, b = inp["x"].to(dev()), inp["bias"].to(dev())
+    old = qlq.qlq_get_skinny_max_m()
+    try:
+        qlq.qlq_set_skinny_max_m(8)
+        y_skinny = qlq.w4a8_linear_forward(x, packed, s, bias=b)
+        qlq.qlq_set_skinny_max_m(0)
+        y_gemm = qlq.w4a8_linear_forward(x, packed, s, bias=b)
+    finally:
+        qlq.qlq_set_skinny_max_m(old)
+    assert torch.equal(y_skinny.view(torch.int16), y_gemm.view(torch.int16))
+    _, _, _, y_ref, D = oracle.w4a8_forward(f32(inp["x"]), oracle.pack_weight_int4(inp["w"].numpy())[0],
+                                            s.cpu().numpy(), bias=f32(inp["bias"]))
+    assert_close(y_skinny, y_ref, D, K, xdt, label=f"w4a8 skinny {xdt} {(M, K, N)}")
