@@ -21,9 +21,13 @@ Readings where the pages are silent (all listed in the design notes):
   * round() is half-to-even (the cider quantizers use ``np.round``);
   * a group whose stored scale is zero (max == min) takes scale 1, following
     the zero-scale guard of the cider quantizers, so its codes are all 0;
-  * codes are packed LSB-first into little-endian uint32 words along K: code k
-    sits at bit ``bits*(k mod (32/bits))`` of word ``k // (32/bits)``;
-  * only widths that divide 32 (1, 2, 4, 8) are packed here.
+  * codes are packed LSB-first into one bit stream per row along K: code k
+    occupies stream bits ``bits*k .. bits*k + bits - 1`` (its least
+    significant bit first), and stream bit i is bit ``i mod 32`` of
+    little-endian uint32 word ``i // 32``.  For widths that divide 32 this
+    puts code k at bit ``bits*(k mod (32/bits))`` of word ``k // (32/bits)``;
+    for 3, 5 and 6 bits a code may straddle two words (the packed width
+    ``input_dims*bits/32`` implies dense packing).
 """
 
 import numpy as np
@@ -31,13 +35,20 @@ import numpy as np
 from .codecs import round_to_dtype
 
 
+BITS = (1, 2, 3, 4, 5, 6, 8)
+
+
+def _check_bits(K, bits):
+    if bits not in BITS:
+        raise ValueError(f"bits={bits} not in {BITS}")
+    if (K * bits) % 32:
+        raise ValueError(f"K={K} does not fill whole uint32 words at {bits} bits")
+
+
 def _check_shape(K, bits, group_size):
-    if bits not in (1, 2, 4, 8):
-        raise ValueError(f"bits={bits} does not divide 32")
     if group_size <= 0 or K % group_size:
         raise ValueError(f"K={K} is not a multiple of group_size={group_size}")
-    if K % (32 // bits):
-        raise ValueError(f"K={K} does not fill whole uint32 words at {bits} bits")
+    _check_bits(K, bits)
 
 
 def affine_quantize(w, bits, group_size, sb_dtype):
@@ -75,33 +86,35 @@ def affine_quantize(w, bits, group_size, sb_dtype):
 
 
 def affine_pack(codes, bits):
-    """Pack codes ``[N, K]`` (each < 2^bits) into uint32 words ``[N, K*bits/32]``."""
+    """Pack codes ``[N, K]`` (each < 2^bits) into uint32 words ``[N, K*bits/32]``.
+
+    Each code is spread into its ``bits`` bits (least significant first), the
+    bits of a row are laid end to end, and every 32 consecutive stream bits
+    form one word (stream bit i -> bit i mod 32 of word i // 32).
+    """
     codes = np.asarray(codes)
     N, K = codes.shape
-    per = 32 // bits
-    if 32 % bits or K % per:
-        raise ValueError("bits must divide 32 and K must fill whole words")
-    if codes.size and int(codes.max()) >= 2 ** bits:
+    _check_bits(K, bits)
+    if codes.size and (int(codes.max()) >= 2 ** bits or int(codes.min()) < 0):
         raise ValueError("code out of range")
-    c = codes.astype(np.uint32).reshape(N, K // per, per)
-    words = np.zeros((N, K // per), dtype=np.uint32)
-    for slot in range(per):
-        words |= c[:, :, slot] << np.uint32(bits * slot)
-    return words
+    t = np.arange(bits, dtype=np.uint32)
+    stream = (codes.astype(np.uint32)[:, :, None] >> t) & np.uint32(1)        # [N, K, bits]
+    stream = stream.reshape(N, K * bits // 32, 32)
+    place = np.uint32(1) << np.arange(32, dtype=np.uint32)
+    return (stream * place).sum(axis=2, dtype=np.uint64).astype(np.uint32)
 
 
 def affine_unpack(words, K, bits):
     """Unpack uint32 words ``[N, K*bits/32]`` into codes uint8 ``[N, K]``."""
     words = np.asarray(words, dtype=np.uint32)
     N = words.shape[0]
-    per = 32 // bits
-    if words.shape[1] * per != K:
+    _check_bits(K, bits)
+    if words.shape[1] * 32 != K * bits:
         raise ValueError("packed width does not match K")
-    mask = np.uint32(2 ** bits - 1)
-    codes = np.empty((N, K // per, per), dtype=np.uint8)
-    for slot in range(per):
-        codes[:, :, slot] = (words >> np.uint32(bits * slot)) & mask
-    return codes.reshape(N, K)
+    stream = (words[:, :, None] >> np.arange(32, dtype=np.uint32)) & np.uint32(1)   # [N, W, 32]
+    stream = stream.reshape(N, K, bits).astype(np.uint32)
+    weight = np.uint32(1) << np.arange(bits, dtype=np.uint32)
+    return (stream * weight).sum(axis=2).astype(np.uint8)
 
 
 def affine_dequantize(codes, scales, biases, group_size):

@@ -34,18 +34,43 @@ def test_bit_order_golden():
 
 def test_pack_unpack_bijection_random_words():
     rng = np.random.default_rng(1)
-    for bits in (1, 2, 4, 8):
-        per = 32 // bits
-        words = rng.integers(0, 1 << 32, size=(5, 7), dtype=np.uint64).astype(np.uint32)
-        codes = affine.affine_unpack(words, 7 * per, bits)
+    for bits in (1, 2, 3, 4, 5, 6, 8):
+        words = rng.integers(0, 1 << 32, size=(5, 7 * bits), dtype=np.uint64).astype(np.uint32)
+        codes = affine.affine_unpack(words, 7 * 32, bits)
         assert codes.max() < 2 ** bits
         assert np.array_equal(affine.affine_pack(codes, bits), words)
 
 
+def test_bitstream_golden():
+    with open(os.path.join(GOLDEN, "affine_bitstream.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        bits = case["bits"]
+        codes = np.array([case["codes"]], dtype=np.uint8)
+        words = np.array([[int(h, 16) for h in case["words_hex"]]], dtype=np.uint32)
+        assert np.array_equal(affine.affine_pack(codes, bits), words), case["note"]
+        assert np.array_equal(affine.affine_unpack(words, codes.shape[1], bits), codes), case["note"]
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
+def test_pack_matches_big_integer_stream(bits):
+    """A row as one Python integer: sum_k q_k * 2^(bits*k); word i is bits
+    32 i .. 32 i + 31 of it."""
+    rng = np.random.default_rng(bits)
+    K = 96
+    codes = rng.integers(0, 2 ** bits, size=(3, K)).astype(np.uint8)
+    words = affine.affine_pack(codes, bits)
+    for n in range(3):
+        v = sum(int(codes[n, k]) << (bits * k) for k in range(K))
+        ref = [(v >> (32 * i)) & 0xFFFFFFFF for i in range(K * bits // 32)]
+        assert [int(u) for u in words[n]] == ref
+
+
 def _python_unpack(word_row, K, bits):
-    """Independent per-element bit extraction, plain Python ints."""
-    per = 32 // bits
-    return [(int(word_row[k // per]) >> (bits * (k % per))) & ((1 << bits) - 1) for k in range(K)]
+    """Independent per-element bit extraction, plain Python ints: the row's
+    words as one integer, code k = its bits bits*k .. bits*k + bits - 1."""
+    v = sum(int(u) << (32 * i) for i, u in enumerate(word_row))
+    return [(v >> (bits * k)) & ((1 << bits) - 1) for k in range(K)]
 
 
 # --------------------------------------------------------- worked quantization
@@ -69,7 +94,8 @@ def test_worked_quantization_golden():
 
 # ------------------------------------------------------- quantizer properties
 CASES = [(4, 64, "f32"), (4, 64, "bf16"), (4, 128, "bf16"), (4, 32, "f16"),
-         (2, 64, "bf16"), (8, 128, "f32"), (8, 32, "bf16"), (1, 32, "f32")]
+         (2, 64, "bf16"), (8, 128, "f32"), (8, 32, "bf16"), (1, 32, "f32"),
+         (3, 64, "bf16"), (3, 32, "f32"), (5, 128, "f16"), (6, 64, "bf16"), (6, 32, "f32")]
 
 
 def _weights(seed, N=24, K=256, std=0.02):
@@ -191,7 +217,7 @@ def test_rejects_bad_input():
     with pytest.raises(ValueError):
         affine.affine_quantize(w, 4, 48, "f32")
     with pytest.raises(ValueError):
-        affine.affine_quantize(w, 3, 32, "f32")
+        affine.affine_quantize(w, 7, 32, "f32")      # 7 bits is not a layer width
     w[0, 3] = np.inf
     with pytest.raises(ValueError):
         affine.affine_quantize(w, 4, 32, "f32")
@@ -215,12 +241,12 @@ def test_dequantize_single_rounding_matches_fp32_fma():
 
 
 # --------------------------------------------------------------- forward pins
-@pytest.mark.parametrize("bits,G", [(2, 8), (4, 8), (8, 8), (4, 16)])
+@pytest.mark.parametrize("bits,G", [(2, 8), (4, 8), (8, 8), (4, 16), (3, 32), (5, 32), (6, 16), (1, 32)])
 def test_forward_brute_force_fractions(bits, G):
-    """M=2, K=16, N=8: packed words unpacked by plain bit arithmetic and the
-    product summed in exact rationals."""
+    """M=2, K=16 or 32, N=8: packed words unpacked by plain bit arithmetic
+    and the product summed in exact rationals."""
     rng = np.random.default_rng(10 + bits)
-    M, K, N = 2, 16, 8
+    M, K, N = 2, max(16, G), 8
     x = rng.standard_normal((M, K)).astype(np.float32)
     w = rng.standard_normal((N, K)).astype(np.float32)
     bias = rng.standard_normal(N).astype(np.float32)
