@@ -80,10 +80,14 @@ int current_device_status() {
     if (!(cond)) return fail(code, __VA_ARGS__); \
   } while (0)
 
+bool affine_bits_ok(int bits) { return (bits >= 1 && bits <= 6) || bits == 8; }
+// widths whose GEMM runs on codes transcoded to the 8-bit layout
+bool transcoded_gemm(int bits) { return bits != 2 && bits != 4 && bits != 8; }
+
 int check_affine_shape(int64_t N, int64_t K, int bits, int G) {
   QLQ_REQUIRE(N >= 1 && K >= 1 && N < kMaxDim && K < kMaxDim, QLQ_ERR_INVALID_ARG,
               "invalid shape N=%lld K=%lld", (long long)N, (long long)K);
-  QLQ_REQUIRE(bits == 2 || bits == 4 || bits == 8, QLQ_ERR_UNSUPPORTED, "bits=%d not built (2, 4, 8)", bits);
+  QLQ_REQUIRE(affine_bits_ok(bits), QLQ_ERR_UNSUPPORTED, "bits=%d not supported (1-6, 8)", bits);
   QLQ_REQUIRE(G == 32 || G == 64 || G == 128, QLQ_ERR_UNSUPPORTED,
               "group_size=%d not built (32, 64, 128)", G);
   QLQ_REQUIRE(K % G == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of group_size=%d", (long long)K, G);
@@ -158,8 +162,8 @@ QLQ_API int qlq_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits, u
                        void* stream) {
   QLQ_REQUIRE(packed && codes, QLQ_ERR_INVALID_ARG, "null pointer");
   QLQ_REQUIRE(N >= 1 && K >= 1 && N < kMaxDim && K < kMaxDim, QLQ_ERR_INVALID_ARG, "invalid shape");
-  QLQ_REQUIRE(bits == 2 || bits == 4 || bits == 8, QLQ_ERR_UNSUPPORTED, "bits=%d", bits);
-  QLQ_REQUIRE(K % (32 / bits) == 0, QLQ_ERR_INVALID_ARG, "K must fill whole words");
+  QLQ_REQUIRE(affine_bits_ok(bits), QLQ_ERR_UNSUPPORTED, "bits=%d not supported (1-6, 8)", bits);
+  QLQ_REQUIRE((K * bits) % 32 == 0, QLQ_ERR_INVALID_ARG, "K must fill whole words");
   QLQ_REQUIRE(aligned(packed, 4), QLQ_ERR_ALIGNMENT, "packed not 4-byte aligned");
   if (int st = current_device_status()) return st;
   return hip_status(qlq::launch_affine_unpack(packed, N, K, bits, codes, (hipStream_t)stream), "unpack");
@@ -181,10 +185,11 @@ QLQ_API int qlq_dequantize(const uint32_t* packed, const void* scales, const voi
 
 QLQ_API size_t qlq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int bits, int group_size,
                                          int x_dtype) {
-  (void)bits;
   if (M <= 0 || K <= 0 || N <= 0 || group_size <= 0 || K % group_size) return 0;
   if (!takes_gemm(M, K, N, group_size, x_dtype)) return 0;
-  return qlq::affine_gemm_workspace(M, K, N, group_size);
+  size_t need = (qlq::affine_gemm_workspace(M, K, N, group_size) + 255) & ~(size_t)255;
+  if (transcoded_gemm(bits)) need += (size_t)N * (size_t)K;  // the codes as bytes (the 8-bit layout)
+  return need;
 }
 
 QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
@@ -202,7 +207,7 @@ QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
               QLQ_ERR_ALIGNMENT, "misaligned scales / biases / bias / y");
   const bool gemm = takes_gemm(M, K, N, group_size, x_dtype);
   if (gemm) {
-    const size_t need = qlq::affine_gemm_workspace(M, K, N, group_size);
+    const size_t need = qlq_linear_workspace_size(M, K, N, bits, group_size, x_dtype);
     QLQ_REQUIRE(workspace && workspace_bytes >= need, QLQ_ERR_WORKSPACE,
                 "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
     QLQ_REQUIRE(aligned(workspace, 256), QLQ_ERR_ALIGNMENT, "workspace not 256-byte aligned");
@@ -212,6 +217,18 @@ QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
   if (M == 0) return ok();
   if (int st = current_device_status()) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (gemm && transcoded_gemm(bits)) {
+    // 1, 3, 5, 6 bits: the codes are unpacked to one byte each, which is the
+    // 8-bit packed layout, and the 8-bit GEMM runs on them with the same
+    // scales and biases
+    uint32_t* codes8 = (uint32_t*)((char*)workspace +
+                                   ((qlq::affine_gemm_workspace(M, K, N, group_size) + 255) & ~(size_t)255));
+    if (int st = hip_status(qlq::launch_affine_unpack(packed, N, K, bits, (uint8_t*)codes8, s), "transcode"))
+      return st;
+    return hip_status(qlq::launch_affine_gemm(x, x_dtype, M, K, codes8, scales, biases, N, 8, group_size, bias,
+                                              y, workspace, s),
+                      "affine gemm");
+  }
   if (gemm)
     return hip_status(qlq::launch_affine_gemm(x, x_dtype, M, K, packed, scales, biases, N, bits, group_size,
                                               bias, y, workspace, s),

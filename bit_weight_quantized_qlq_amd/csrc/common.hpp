@@ -241,4 +241,24 @@ struct RowDivider {
   }
 };
 
+// ------------------------------------------------ affine n-bit code streams
+// A row's codes form one LSB-first bit stream (code k at stream bits
+// BITS*k .. BITS*k + BITS - 1, stream bit i = bit i % 32 of word i / 32), so
+// 32 codes always fill exactly BITS words: a unit.  With j known at compile
+// time the offsets fold away; a code that straddles two words (3, 5, 6 bits)
+// is one funnel shift.
+template <int BITS>
+__device__ __forceinline__ uint32_t unit_code(const uint32_t* w, int j) {
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  const int p = BITS * j, i = p >> 5, o = p & 31;
+  if (o + BITS <= 32) return (w[i] >> o) & mask;
+  return ((w[i] >> o) | (w[i + 1] << (32 - o))) & mask;
+}
+template <int BITS>
+__device__ __forceinline__ void unit_put(uint32_t* w, int j, uint32_t q) {
+  const int p = BITS * j, i = p >> 5, o = p & 31;
+  w[i] |= q << o;
+  if (o + BITS > 32) w[i + 1] |= q >> (32 - o);
+}
+
 }  // namespace qlq

@@ -60,23 +60,29 @@ template <> struct PairTraits<f16_t> {
   }
 };
 
-// Codes per chunk: 32 for 2- and 4-bit codes (8 or 16 bytes), 16 for 8-bit.
+// Codes per chunk: one unit of 32 codes (BITS words) for 1- to 6-bit codes,
+// 16 for 8-bit (4 words).
 template <int BITS> struct Chunk {
   static constexpr int CODES = BITS == 8 ? 16 : 32;
-  static constexpr int WORDS = CODES * BITS / 32;  // 2, 4 or 4
+  static constexpr int WORDS = CODES * BITS / 32;  // BITS, or 4 at 8 bits
 };
 
 template <int WORDS> struct WordsT { uint32_t w[WORDS]; };
 
+// a chunk's words; 16- and 8-byte chunks are one load (their offsets are
+// multiples of their size), 3-, 5- and 6-word chunks are dword loads
 template <int WORDS>
 __device__ __forceinline__ WordsT<WORDS> load_words(const uint32_t* p) {
   WordsT<WORDS> r;
   if constexpr (WORDS == 4) {
     uint4 v = *reinterpret_cast<const uint4*>(p);
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-  } else {
+  } else if constexpr (WORDS == 2) {
     uint2 v = *reinterpret_cast<const uint2*>(p);
     r.w[0] = v.x; r.w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) r.w[i] = p[i];
   }
   return r;
 }
@@ -379,7 +385,8 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
 }
 
 // ---------------------------------------------------------------------------
-// Generic path: any x dtype and bit width; code -> fp32, fp32 FMA.
+// Generic path: any x dtype and bit width; code -> fp32, fp32 FMA.  Codes
+// come out of the chunk's bit stream at compile-time offsets.
 // ---------------------------------------------------------------------------
 template <int BITS, typename XT, int MT, int R>
 __global__ void __launch_bounds__(64 * QLQ_GEMV_WAVES_PER_BLOCK)
@@ -388,13 +395,12 @@ gemv_generic_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32
                     const XT* __restrict__ bias, XT* __restrict__ y) {
   constexpr int CODES = Chunk<BITS>::CODES;
   constexpr int WORDS = Chunk<BITS>::WORDS;
-  constexpr int PER = 32 / BITS;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = (int64_t)blockIdx.x * QLQ_GEMV_WAVES_PER_BLOCK + (threadIdx.x >> 6);
   const int64_t n0 = wave * R;
   if (n0 >= N) return;
   const int64_t m0 = (int64_t)blockIdx.y * MT;
-  const int64_t cpr = K / CODES, wpr = K / PER, gpr = K / G;
+  const int64_t cpr = K / CODES, wpr = K * BITS / 32, gpr = K / G;
 
   float acc[MT][R];
 #pragma unroll
@@ -428,10 +434,7 @@ gemv_generic_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32
       for (int r = 0; r < R; ++r) {
         float P = 0.0f;
 #pragma unroll
-        for (int t = 0; t < WORDS; ++t)
-#pragma unroll
-          for (int j = 0; j < PER; ++j)
-            P = __fmaf_rn(xv[t * PER + j], (float)((wv[r].w[t] >> (BITS * j)) & ((1u << BITS) - 1u)), P);
+        for (int i = 0; i < CODES; ++i) P = __fmaf_rn(xv[i], (float)unit_code<BITS>(wv[r].w, i), P);
         acc[m][r] = __fmaf_rn(s[r], P, __fmaf_rn(b[r], X, acc[m][r]));
       }
     }
@@ -516,8 +519,12 @@ hipError_t launch_affine_gemv(const void* x, int x_dtype, int64_t M, int64_t K,
                               const uint32_t* packed, const void* scales, const void* biases,
                               int64_t N, int bits, int G, const void* bias, void* y, hipStream_t s) {
   switch (bits) {
+    case 1: return gemv_dispatch_x<1>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, s);
     case 2: return gemv_dispatch_x<2>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, s);
+    case 3: return gemv_dispatch_x<3>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, s);
     case 4: return gemv_dispatch_x<4>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, s);
+    case 5: return gemv_dispatch_x<5>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, s);
+    case 6: return gemv_dispatch_x<6>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, s);
     default: return gemv_dispatch_x<8>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, s);
   }
 }

@@ -20,7 +20,8 @@ namespace qlq {
 
 // ---------------------------------------------------------------- affine pack
 // One thread per (row n, group g).  The thread reads its G weights, forms the
-// fp32 min/max, the stored scale and bias, and writes G*bits/32 packed words.
+// fp32 min/max, the stored scale and bias, and writes the group's G/32 units
+// of BITS words (32 codes each; G is a multiple of 32).
 template <int BITS, typename SB>
 __global__ void __launch_bounds__(256)
 affine_pack_kernel(const float* __restrict__ w, int64_t N, int64_t K, int G,
@@ -51,17 +52,19 @@ affine_pack_kernel(const float* __restrict__ w, int64_t N, int64_t K, int G,
   Elem<SB>::store(scales, t, s);
   Elem<SB>::store(biases, t, b);
 
-  constexpr int per = 32 / BITS;
-  uint32_t* out = packed + (n * K + g * G) / per;
-  for (int i = 0; i < G; i += per) {
-    uint32_t word = 0;
+  uint32_t* out = packed + (n * K + g * G) / 32 * BITS;
+  for (int u = 0; u < G / 32; ++u) {
+    uint32_t wd[BITS];
 #pragma unroll
-    for (int j = 0; j < per; ++j) {
-      float q = rintf(__fdiv_rn(__fsub_rn(wg[i + j], b), s));
+    for (int i = 0; i < BITS; ++i) wd[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      float q = rintf(__fdiv_rn(__fsub_rn(wg[32 * u + j], b), s));
       q = fminf(fmaxf(q, 0.0f), (float)qmax);
-      word |= (uint32_t)q << (BITS * j);
+      unit_put<BITS>(wd, j, (uint32_t)q);
     }
-    out[i / per] = word;
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) out[u * BITS + i] = wd[i];
   }
 }
 
@@ -87,66 +90,100 @@ static hipError_t pack_dispatch_sb(const float* w, int64_t N, int64_t K, int G, 
   return hipGetLastError();
 }
 
+// every affine bit width the layer supports
+#define QLQ_AFFINE_BITS_SWITCH(bits, CALL) \
+  switch (bits) {                          \
+    case 1: return CALL(1);                \
+    case 2: return CALL(2);                \
+    case 3: return CALL(3);                \
+    case 4: return CALL(4);                \
+    case 5: return CALL(5);                \
+    case 6: return CALL(6);                \
+    default: return CALL(8);               \
+  }
+
 hipError_t launch_affine_pack(const float* w, int64_t N, int64_t K, int bits, int G,
                               uint32_t* packed, void* scales, void* biases, int sb_dtype,
                               int* err_flag, hipStream_t s) {
-  switch (bits) {
-    case 2: return pack_dispatch_sb<2>(w, N, K, G, packed, scales, biases, sb_dtype, err_flag, s);
-    case 4: return pack_dispatch_sb<4>(w, N, K, G, packed, scales, biases, sb_dtype, err_flag, s);
-    default: return pack_dispatch_sb<8>(w, N, K, G, packed, scales, biases, sb_dtype, err_flag, s);
-  }
+#define QLQ_CALL(B) pack_dispatch_sb<B>(w, N, K, G, packed, scales, biases, sb_dtype, err_flag, s)
+  QLQ_AFFINE_BITS_SWITCH(bits, QLQ_CALL)
+#undef QLQ_CALL
 }
 
 // -------------------------------------------------------------- affine unpack
-template <int BITS>
+// The rows of a packed matrix are whole words, so all N*K codes form one
+// stream; a thread takes one unit of 32 codes (the last may be partial).
+// VEC: codes 16-byte aligned and N*K % 32 == 0, two 16-byte stores per unit.
+template <int BITS, bool VEC>
 __global__ void __launch_bounds__(256)
-affine_unpack_kernel(const uint32_t* __restrict__ packed, int64_t nwords, uint8_t* __restrict__ codes) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= nwords) return;
-  constexpr int per = 32 / BITS;
-  const uint32_t word = packed[t];
+affine_unpack_kernel(const uint32_t* __restrict__ packed, int64_t ncodes, uint8_t* __restrict__ codes) {
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t k0 = u * 32;
+  if (k0 >= ncodes) return;
+  const int64_t nwords = ncodes * BITS / 32;
+  uint32_t wd[BITS];
 #pragma unroll
-  for (int j = 0; j < per; ++j) codes[t * per + j] = (uint8_t)((word >> (BITS * j)) & ((1u << BITS) - 1u));
+  for (int i = 0; i < BITS; ++i) wd[i] = u * BITS + i < nwords ? packed[u * BITS + i] : 0u;
+  if constexpr (VEC) {
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o[i] = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[i] |= unit_code<BITS>(wd, 4 * i + j) << (8 * j);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(codes + k0);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (k0 + j < ncodes) codes[k0 + j] = (uint8_t)unit_code<BITS>(wd, j);
+  }
+}
+
+template <int BITS>
+static hipError_t unpack_dispatch(const uint32_t* packed, int64_t ncodes, uint8_t* codes, hipStream_t s) {
+  dim3 grid((unsigned)cdiv(cdiv(ncodes, 32), 256)), block(256);
+  if (ncodes % 32 == 0 && ((uintptr_t)codes & 15) == 0)
+    hipLaunchKernelGGL((affine_unpack_kernel<BITS, true>), grid, block, 0, s, packed, ncodes, codes);
+  else
+    hipLaunchKernelGGL((affine_unpack_kernel<BITS, false>), grid, block, 0, s, packed, ncodes, codes);
+  return hipGetLastError();
 }
 
 hipError_t launch_affine_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits,
                                 uint8_t* codes, hipStream_t s) {
-  const int64_t nwords = N * K * bits / 32;
-  dim3 grid((unsigned)cdiv(nwords, 256)), block(256);
-  switch (bits) {
-    case 2: hipLaunchKernelGGL(affine_unpack_kernel<2>, grid, block, 0, s, packed, nwords, codes); break;
-    case 4: hipLaunchKernelGGL(affine_unpack_kernel<4>, grid, block, 0, s, packed, nwords, codes); break;
-    default: hipLaunchKernelGGL(affine_unpack_kernel<8>, grid, block, 0, s, packed, nwords, codes); break;
-  }
-  return hipGetLastError();
+#define QLQ_CALL(B) unpack_dispatch<B>(packed, N * K, codes, s)
+  QLQ_AFFINE_BITS_SWITCH(bits, QLQ_CALL)
+#undef QLQ_CALL
 }
 
 // ----------------------------------------------------------- affine dequantize
-// w = fma(scale, q, bias): one rounding of the exact value, in fp32.
+// w = fma(scale, q, bias): one rounding of the exact value, in fp32.  One
+// thread per unit of 32 codes (a unit never straddles a group: G % 32 == 0).
 template <int BITS, typename SB>
 __global__ void __launch_bounds__(256)
 affine_dequant_kernel(const uint32_t* __restrict__ packed, const SB* __restrict__ scales,
                       const SB* __restrict__ biases, int64_t N, int64_t K, int G,
                       float* __restrict__ w) {
-  constexpr int per = 32 / BITS;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t words_per_row = K / per;
-  if (t >= N * words_per_row) return;
-  const int64_t n = t / words_per_row, k0 = (t % words_per_row) * per;
-  const int64_t gi = n * (K / G) + k0 / G;  // a word never straddles a group (G % per == 0)
+  const int64_t units_per_row = K / 32;
+  if (t >= N * units_per_row) return;
+  const int64_t n = t / units_per_row, k0 = (t % units_per_row) * 32;
+  const int64_t gi = n * (K / G) + k0 / G;
   const float s = Elem<SB>::load(scales, gi), b = Elem<SB>::load(biases, gi);
-  const uint32_t word = packed[t];
+  uint32_t wd[BITS];
 #pragma unroll
-  for (int j = 0; j < per; ++j) {
-    const float q = (float)((word >> (BITS * j)) & ((1u << BITS) - 1u));
-    w[n * K + k0 + j] = __fmaf_rn(s, q, b);
-  }
+  for (int i = 0; i < BITS; ++i) wd[i] = packed[t * BITS + i];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) w[n * K + k0 + j] = __fmaf_rn(s, (float)unit_code<BITS>(wd, j), b);
 }
 
 template <int BITS>
 static hipError_t dequant_dispatch_sb(const uint32_t* packed, const void* scales, const void* biases,
                                       int sb, int64_t N, int64_t K, int G, float* w, hipStream_t s) {
-  const int64_t total = N * K * BITS / 32;
+  const int64_t total = N * (K / 32);
   dim3 grid((unsigned)cdiv(total, 256)), block(256);
   switch (sb) {
     case F32:
@@ -168,11 +205,9 @@ static hipError_t dequant_dispatch_sb(const uint32_t* packed, const void* scales
 hipError_t launch_affine_dequant(const uint32_t* packed, const void* scales, const void* biases,
                                  int sb_dtype, int64_t N, int64_t K, int bits, int G, float* w,
                                  hipStream_t s) {
-  switch (bits) {
-    case 2: return dequant_dispatch_sb<2>(packed, scales, biases, sb_dtype, N, K, G, w, s);
-    case 4: return dequant_dispatch_sb<4>(packed, scales, biases, sb_dtype, N, K, G, w, s);
-    default: return dequant_dispatch_sb<8>(packed, scales, biases, sb_dtype, N, K, G, w, s);
-  }
+#define QLQ_CALL(B) dequant_dispatch_sb<B>(packed, scales, biases, sb_dtype, N, K, G, w, s)
+  QLQ_AFFINE_BITS_SWITCH(bits, QLQ_CALL)
+#undef QLQ_CALL
 }
 
 // ---------------------------------------------------------------- ternary pack
@@ -473,29 +508,37 @@ hipError_t launch_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int6
 // in the high nibble, and scale [N] fp32: s = absmax of the column / 7 (1 if
 // 0), code = clamp(rint(w / s) + 8, 0, 15), the quotient correctly rounded.
 // A block covers 64 consecutive columns (a wave reads 64 neighbours of one
-// row) with its four waves splitting the rows: pass 1 takes each wave's
-// column maxima over rows k = wave, wave + 4, ..., LDS joins the four; pass 2
-// writes k-pair rows kp = wave, wave + 4, ...
+// row) with its sixteen waves splitting the rows: pass 1 takes each wave's
+// column maxima over rows k = wave, wave + 16, ..., LDS joins the sixteen;
+// pass 2 writes k-pair rows kp = wave, wave + 16, ...  Loops are unrolled so
+// that eight loads are in flight per lane.
+constexpr int kPackInt4Slices = 16;
 template <typename T>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * kPackInt4Slices)
 pack_int4_cols_kernel(const T* __restrict__ w, int K, int N, uint8_t* __restrict__ packed,
                       float* __restrict__ scale) {
-  __shared__ float red[4][64];
+  constexpr int SL = kPackInt4Slices;
+  __shared__ float red[SL][64];
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const int n = blockIdx.x * 64 + tx;
   const bool in = n < N;
   float a = 0.0f;
-  if (in)
-    for (int k = ty; k < K; k += 4) a = fmaxf(a, fabsf(Elem<T>::load(w, (int64_t)k * N + n)));
+  if (in) {
+#pragma unroll 8
+    for (int k = ty; k < K; k += SL) a = fmaxf(a, fabsf(Elem<T>::load(w, (int64_t)k * N + n)));
+  }
   red[ty][tx] = a;
   __syncthreads();
-  a = fmaxf(fmaxf(red[0][tx], red[1][tx]), fmaxf(red[2][tx], red[3][tx]));
+  a = red[0][tx];
+#pragma unroll
+  for (int i = 1; i < SL; ++i) a = fmaxf(a, red[i][tx]);
   float sc = __fdiv_rn(a, 7.0f);
   if (sc == 0.0f) sc = 1.0f;
   if (!in) return;
   if (ty == 0) scale[n] = sc;
   const RowDivider dv(sc);
-  for (int kp = ty; kp < K / 2; kp += 4) {
+#pragma unroll 4
+  for (int kp = ty; kp < K / 2; kp += SL) {
     const float h = fminf(fmaxf(rintf(dv.div(Elem<T>::load(w, (int64_t)(2 * kp) * N + n))) + 8.0f, 0.0f), 15.0f);
     const float l = fminf(fmaxf(rintf(dv.div(Elem<T>::load(w, (int64_t)(2 * kp + 1) * N + n))) + 8.0f, 0.0f), 15.0f);
     packed[(int64_t)kp * N + n] = (uint8_t)(((int)h << 4) | (int)l);
@@ -504,7 +547,7 @@ pack_int4_cols_kernel(const T* __restrict__ w, int K, int N, uint8_t* __restrict
 
 hipError_t launch_pack_int4_cols(const void* w, int w_dtype, int64_t K, int64_t N, uint8_t* packed, float* scale,
                                  hipStream_t s) {
-  const dim3 grid((unsigned)cdiv(N, 64)), block(256);
+  const dim3 grid((unsigned)cdiv(N, 64)), block(64 * kPackInt4Slices);
   switch (w_dtype) {
     case F32:
       hipLaunchKernelGGL(pack_int4_cols_kernel<float>, grid, block, 0, s, (const float*)w, (int)K, (int)N, packed,

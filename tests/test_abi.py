@@ -62,8 +62,8 @@ def _lin(**kw):
     (dict(M=-1), qlq.QLQ_ERR_INVALID_ARG),
     (dict(N=0), qlq.QLQ_ERR_INVALID_ARG),
     (dict(K=250), qlq.QLQ_ERR_INVALID_ARG),          # K % G != 0
-    (dict(bits=3), qlq.QLQ_ERR_UNSUPPORTED),
-    (dict(bits=5), qlq.QLQ_ERR_UNSUPPORTED),
+    (dict(bits=7), qlq.QLQ_ERR_UNSUPPORTED),     # layer widths are 1-6 and 8
+    (dict(bits=0), qlq.QLQ_ERR_UNSUPPORTED),
     (dict(G=48), qlq.QLQ_ERR_UNSUPPORTED),
     (dict(G=256, K=512), qlq.QLQ_ERR_UNSUPPORTED),
     (dict(x_dtype=7, sb_dtype=7), qlq.QLQ_ERR_UNSUPPORTED),
@@ -79,6 +79,14 @@ def test_linear_forward_validation(kw, code):
     assert qlq.last_error() != ""
 
 
+def test_transcoded_widths_need_room_for_byte_codes():
+    L = qlq.lib()
+    base = L.qlq_linear_workspace_size(2048, 4096, 11008, 4, 128, qlq.QLQ_BF16)
+    for bits in (1, 3, 5, 6):
+        assert L.qlq_linear_workspace_size(2048, 4096, 11008, bits, 128, qlq.QLQ_BF16) >= base + 11008 * 4096
+    assert L.qlq_linear_workspace_size(4, 4096, 11008, 3, 128, qlq.QLQ_BF16) == 0   # skinny: none
+
+
 def test_workspace_sizes():
     L = qlq.lib()
     # skinny path needs none; GEMM path needs the group-sum split
@@ -92,7 +100,7 @@ def test_workspace_sizes():
 
 @pytest.mark.parametrize("args,code", [
     ((None, 8, 64, 4, 64, A, A, A, qlq.QLQ_BF16, None), qlq.QLQ_ERR_INVALID_ARG),
-    ((A, 8, 64, 3, 64, A, A, A, qlq.QLQ_BF16, None), qlq.QLQ_ERR_UNSUPPORTED),
+    ((A, 8, 64, 7, 64, A, A, A, qlq.QLQ_BF16, None), qlq.QLQ_ERR_UNSUPPORTED),
     ((A, 8, 64, 4, 16, A, A, A, qlq.QLQ_BF16, None), qlq.QLQ_ERR_UNSUPPORTED),
     ((A, 8, 96, 4, 64, A, A, A, qlq.QLQ_BF16, None), qlq.QLQ_ERR_INVALID_ARG),
     ((A, 8, 64, 4, 64, A, A, A, 9, None), qlq.QLQ_ERR_UNSUPPORTED),
@@ -147,7 +155,8 @@ def test_int8_helpers_validation():
     assert L.qlq_int8_matmul_int32(ODD, B, 4, 4, 64, A, None) == qlq.QLQ_ERR_ALIGNMENT
     assert L.qlq_quantize_rows_int8(A, qlq.QLQ_F16, 4, 40, A, A, None) == qlq.QLQ_ERR_INVALID_ARG
     assert L.qlq_quantize_rows_int8(A, 11, 4, 64, A, A, None) == qlq.QLQ_ERR_UNSUPPORTED
-    assert L.qlq_unpack(A, 4, 64, 3, A, None) == qlq.QLQ_ERR_UNSUPPORTED
+    assert L.qlq_unpack(A, 4, 64, 7, A, None) == qlq.QLQ_ERR_UNSUPPORTED
+    assert L.qlq_unpack(A, 4, 40, 3, A, None) == qlq.QLQ_ERR_INVALID_ARG    # 120 bits: not whole words
     assert L.qlq_dequantize(A, A, A, qlq.QLQ_BF16, 4, 64, 4, 48, A, None) == qlq.QLQ_ERR_UNSUPPORTED
 
 

@@ -38,7 +38,7 @@ def test_pack_bitexact_workloads(name):
     _assert_pack_equal(gpu, ref, cfg["bits"])
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("sb", [torch.float32, torch.float16, torch.bfloat16])
 def test_pack_bitexact_variants(bits, G, sb):
@@ -72,10 +72,12 @@ def test_pack_rejects_non_finite():
     assert e.value.code == qlq.QLQ_ERR_DATA
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
-def test_unpack_bitexact(bits):
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("N,K", [(33, 512), (7, 48)])   # 7 x 48 codes: a partial last unit at 2 bits
+def test_unpack_bitexact(bits, N, K):
+    if (K * bits) % 32:
+        pytest.skip("rows must be whole words")
     rng = np.random.default_rng(40 + bits)
-    N, K = 33, 512
     words = rng.integers(0, 1 << 32, size=(N, K * bits // 32), dtype=np.uint64).astype(np.uint32)
     packed = torch.from_numpy(words.view(np.int32)).to(dev())
     codes = qlq.qlq_unpack(packed, K, bits)
@@ -83,7 +85,9 @@ def test_unpack_bitexact(bits):
 
 
 @pytest.mark.parametrize("bits,G,sb", [(4, 64, torch.bfloat16), (4, 128, torch.float16),
-                                       (2, 32, torch.float32), (8, 64, torch.bfloat16)])
+                                       (2, 32, torch.float32), (8, 64, torch.bfloat16),
+                                       (3, 64, torch.bfloat16), (5, 32, torch.float32),
+                                       (6, 128, torch.float16), (1, 64, torch.bfloat16)])
 def test_dequantize_bitexact(bits, G, sb):
     w = workloads.affine_inputs(1, 512, 29, seed=7)["w"]
     (packed, scales, biases), (codes, s_ref, b_ref) = _pack_both(w, bits, G, sb)
@@ -135,6 +139,10 @@ SHAPES = [  # (M, K, N, bits, G)
     (1, 416, 200, 4, 32), (2, 448, 130, 4, 64), (3, 640, 77, 4, 128), (5, 448, 64, 2, 64),
     (8, 384, 129, 8, 128), (9, 416, 200, 4, 32), (17, 448, 250, 2, 64), (33, 640, 131, 4, 128),
     (130, 384, 257, 8, 64), (1, 4096, 96, 4, 64), (20, 416, 72, 2, 32), (40, 4160, 72, 4, 64),
+    # code streams that straddle words (3, 5, 6 bits) and 1 bit; the GEMM
+    # path runs them on codes transcoded to bytes
+    (1, 416, 200, 3, 32), (3, 640, 77, 5, 128), (9, 448, 130, 6, 64), (17, 384, 129, 1, 128),
+    (130, 384, 257, 3, 64), (40, 4160, 72, 5, 64), (33, 640, 131, 6, 128), (20, 448, 250, 1, 32),
 ]
 
 
@@ -159,7 +167,7 @@ def test_forward_paths_ragged(path, xdt, shape):
 # (two blocks per compute unit; 2- and 8-bit codes keep 128-row blocks); M is
 # ragged against 256 and N against 128
 TALL_SHAPES = [(300, 128, 32808, 4, 32), (520, 256, 32808, 4, 128), (300, 192, 32808, 2, 64),
-               (260, 128, 32808, 8, 128)]
+               (260, 128, 32808, 8, 128), (260, 128, 32808, 3, 32)]
 
 
 @pytest.mark.parametrize("shape", TALL_SHAPES)
