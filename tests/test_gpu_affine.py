@@ -113,7 +113,7 @@ def _forward_case(inp, bits, G, x_dtype, rows=None):
     return yg, y_ref, D
 
 
-@pytest.mark.parametrize("name", ["tiny_affine_4bit", "decode_gemv_4bit"])
+@pytest.mark.parametrize("name", ["tiny_affine_4bit", "decode_gemv_4bit", "decode_gemv_3bit"])
 def test_forward_workloads_skinny(name):
     cfg = workloads.WORKLOADS[name]
     inp = workloads.workload_inputs(name)
@@ -122,10 +122,10 @@ def test_forward_workloads_skinny(name):
     assert_close(y, y_ref, D, cfg["K"], xdt, strict=True, label=name)
 
 
-def test_forward_prefill_full_sampled_rows():
+@pytest.mark.parametrize("name", ["prefill_gemm_4bit", "prefill_gemm_3bit"])
+def test_forward_prefill_full_sampled_rows(name):
     """Full prefill workload through the GEMM kernel; the oracle checks a
     sample of rows (first, last, and spread across tiles) against all N."""
-    name = "prefill_gemm_4bit"
     cfg = workloads.WORKLOADS[name]
     assert cfg["M"] > qlq.qlq_get_skinny_max_m()
     inp = workloads.workload_inputs(name)

@@ -28,8 +28,11 @@ round-to-nearest-even conversion):
                       outlier count and factor); W f32 [K=4096, N=4096]
                       ~N(0,0.02) drawn in the [K, N] orientation the int4
                       packer takes; no bias
+  decode_gemv_3bit    the decode_gemv_4bit recipe with 3-bit codes (a code
+                      stream whose codes straddle words)
+  prefill_gemm_3bit   the prefill_gemm_4bit recipe with 3-bit codes
 
-The default seed of a workload is 1000 + its index in the list above (1..7).
+The default seed of a workload is 1000 + its index in the list above (1..9).
 Smaller parity cases reuse the same recipes at other shapes and seeds.
 """
 
@@ -58,6 +61,12 @@ WORKLOADS = {
     "w4a8_perchannel": dict(index=7, kind="w4a8", M=1024, K=4096, N=4096,
                             x_dtype="f16", bias=False, outlier_frac=0.001,
                             outlier_mult=20.0),
+    "decode_gemv_3bit": dict(index=8, kind="affine", M=1, K=4096, N=4096, bits=3,
+                             group_size=64, x_dtype="bf16", sb_dtype="bf16",
+                             bias=False),
+    "prefill_gemm_3bit": dict(index=9, kind="affine", M=2048, K=4096, N=11008,
+                              bits=3, group_size=128, x_dtype="bf16",
+                              sb_dtype="bf16", bias=True),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
