@@ -34,7 +34,7 @@ from .affine import (
     affine_forward,
 )
 from .ternary import ternary_pack, ternary_unpack, ternary_forward
-from .int8 import quantize_rows_int8, int8_matmul_int32, w8a8_forward
+from .int8 import quantize_rows_int8, quantize_rows_int8_clip, row_percentile, int8_matmul_int32, w8a8_forward
 from .pergroup import quantize_groups_int8, pergroup_forward
 from .w4a8 import pack_weight_int4, unpack_weight_int4, w4a8_forward
 from .tolerance import tolerance, compare
@@ -54,6 +54,8 @@ __all__ = [
     "ternary_unpack",
     "ternary_forward",
     "quantize_rows_int8",
+    "quantize_rows_int8_clip",
+    "row_percentile",
     "int8_matmul_int32",
     "w8a8_forward",
     "quantize_groups_int8",

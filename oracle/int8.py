@@ -12,6 +12,19 @@ Source: "cider/ops.py".
   * ``int8_matmul_int32``: int8 ``a [M, K]`` times int8 ``b [N, K]`` (the
     transposed weight layout) to int32 ``[M, N]``, bit-exact.
 
+  * ``quantize_weight_int8`` with ``clip_percentile`` set: the row's scale
+    comes from the given percentile of |w| instead of its maximum (a zero
+    percentile falls back to the maximum), the row is clipped to
+    [-clip, clip], then quantized with scale = clip / 127 as above.
+
+Reading of the percentile: NumPy's default ("linear") percentile on the
+fp32 array of |w| under NumPy 2 promotion rules, so every step stays in fp32:
+the fraction q = fl32(p / 100), the virtual index v = fl32((K - 1) q), its
+floor i and weight t = v - i, and with the sorted values a <= b at i and
+i + 1: a + (b - a) t when t < 0.5, else b - (b - a)(1 - t), each operation
+rounded to fp32; v >= K - 1 gives the largest value.  (Under NumPy 1 value
+casting the same call computes in fp64.)
+
 Reading: the pages name the activation quantizer ``quant_a`` without defining
 it; it is taken to be the same per-row symmetric absmax/127 rule as the weight
 quantizer, applied to each row of x.  The W8A8 reference output is the product
@@ -36,6 +49,46 @@ def quantize_rows_int8(v):
     s = (a / np.float32(127.0)).astype(np.float32)
     s = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
     q = np.clip(np.rint(v / s[:, None]), -128, 127).astype(np.int8)
+    return q, s
+
+
+def row_percentile(v, percentile):
+    """fp32 percentile of each row of ``v`` (see the module reading)."""
+    v = np.asarray(v, dtype=np.float32)
+    R, K = v.shape
+    srt = np.sort(v, axis=1)
+    q = np.float32(np.float32(percentile) / np.float32(100.0))
+    vi = np.float32(np.float32(K - 1) * q)
+    if vi >= K - 1:
+        return srt[:, K - 1].copy()
+    i = int(np.floor(vi))
+    t = np.float32(vi - np.float32(i))
+    a, b = srt[:, i], srt[:, i + 1]
+    d = (b - a).astype(np.float32)
+    if t >= 0.5:
+        return (b - (d * np.float32(np.float32(1.0) - t)).astype(np.float32)).astype(np.float32)
+    return (a + (d * t).astype(np.float32)).astype(np.float32)
+
+
+def quantize_rows_int8_clip(w, clip_percentile):
+    """Per-row symmetric int8 with a percentile clip (fp32 steps).
+
+    Returns ``(q int8 [R, K], scale f32 [R])``.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    if w.ndim != 2 or w.shape[1] == 0:
+        raise ValueError("expected a non-empty 2-D array")
+    if not np.isfinite(w).all():
+        raise ValueError("non-finite value")
+    if not 0.0 <= clip_percentile <= 100.0:
+        raise ValueError("percentile outside [0, 100]")
+    aw = np.abs(w)
+    clip = row_percentile(aw, clip_percentile)
+    clip = np.where(clip == 0, aw.max(axis=1), clip).astype(np.float32)
+    s = (clip / np.float32(127.0)).astype(np.float32)
+    s = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+    wc = np.clip(w, -clip[:, None], clip[:, None])
+    q = np.clip(np.rint(wc / s[:, None]), -128, 127).astype(np.int8)
     return q, s
 
 
