@@ -18,7 +18,7 @@ from .binding import (  # noqa: F401
     qlq_pack, qlq_unpack, qlq_dequantize, qlq_linear_workspace_size, qlq_linear_forward,
     qlq_set_skinny_max_m, qlq_get_skinny_max_m,
     bitlinear_pack, bitlinear_forward,
-    qlq_quantize_rows_int8, qlq_int8_matmul_int32, w8a8_workspace_size, w8a8_linear_forward,
+    qlq_quantize_rows_int8, qlq_quantize_rows_int8_clip, qlq_int8_matmul_int32, w8a8_workspace_size, w8a8_linear_forward,
     qlq_quantize_groups_int8, pergroup_workspace_size, pergroup_linear_forward,
     w4a8_pack_weight_int4, w4a8_workspace_size, w4a8_linear_forward,
     qlq_device_check, qlq_version,

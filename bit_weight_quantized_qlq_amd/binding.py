@@ -50,6 +50,7 @@ SIGNATURES = {
     "bitlinear_pack": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "bitlinear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _i64, _vp, _int, _vp, _vp, _vp]),
     "qlq_quantize_rows_int8": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp]),
+    "qlq_quantize_rows_int8_clip": (_int, [_vp, _int, _i64, _i64, ctypes.c_float, _vp, _vp, _vp]),
     "qlq_int8_matmul_int32": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "w8a8_workspace_size": (_sz, [_i64, _i64]),
     "w8a8_linear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
@@ -228,6 +229,17 @@ def qlq_quantize_rows_int8(v):
     q = torch.empty((R, K), dtype=torch.int8, device=v.device)
     s = torch.empty((R,), dtype=torch.float32, device=v.device)
     _check(lib().qlq_quantize_rows_int8(_ptr(v), DTYPE_CODE[v.dtype], R, K, _ptr(q), _ptr(s), _stream(v)))
+    return q, s
+
+
+def qlq_quantize_rows_int8_clip(v, clip_percentile):
+    """Per-row int8 with the clip at a percentile of |v|: v [R, K] -> (q int8, scale f32 [R])."""
+    _dev(v, "v", tuple(DTYPE_CODE), 2)
+    R, K = v.shape
+    q = torch.empty((R, K), dtype=torch.int8, device=v.device)
+    s = torch.empty((R,), dtype=torch.float32, device=v.device)
+    _check(lib().qlq_quantize_rows_int8_clip(_ptr(v), DTYPE_CODE[v.dtype], R, K, float(clip_percentile), _ptr(q),
+                                             _ptr(s), _stream(v)))
     return q, s
 
 

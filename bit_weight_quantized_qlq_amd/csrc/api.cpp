@@ -294,6 +294,23 @@ QLQ_API int qlq_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_
                     "quantize rows");
 }
 
+QLQ_API int qlq_quantize_rows_int8_clip(const void* v, int v_dtype, int64_t R, int64_t K, float clip_percentile,
+                                        int8_t* q, float* scale, void* stream) {
+  QLQ_REQUIRE(v && q && scale, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(R >= 0 && R < kMaxDim && K >= 1, QLQ_ERR_INVALID_ARG, "invalid shape");
+  QLQ_REQUIRE(K <= qlq::kClipMaxKHost, QLQ_ERR_UNSUPPORTED, "K=%lld above %lld (rows are sorted on chip)",
+              (long long)K, (long long)qlq::kClipMaxKHost);
+  QLQ_REQUIRE(clip_percentile >= 0.0f && clip_percentile <= 100.0f, QLQ_ERR_INVALID_ARG,
+              "clip_percentile outside [0, 100]");
+  QLQ_REQUIRE(dtype_ok(v_dtype), QLQ_ERR_UNSUPPORTED, "v_dtype %d", v_dtype);
+  QLQ_REQUIRE(aligned(v, dtype_size(v_dtype)) && aligned(scale, 4), QLQ_ERR_ALIGNMENT, "misaligned pointer");
+  if (R == 0) return ok();
+  if (int st = current_device_status()) return st;
+  return hip_status(qlq::launch_quantize_rows_int8_clip(v, v_dtype, R, K, clip_percentile, q, scale,
+                                                        (hipStream_t)stream),
+                    "quantize rows (percentile clip)");
+}
+
 QLQ_API int qlq_int8_matmul_int32(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K, int32_t* c,
                                   void* stream) {
   QLQ_REQUIRE(a && b && c, QLQ_ERR_INVALID_ARG, "null pointer");

@@ -23,6 +23,10 @@ hipError_t launch_ternary_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* p
 // unpack to (high nibbles then low nibbles, four bytes at a time)
 hipError_t launch_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_t K,
                                      int8_t* q, float* scale, hipStream_t s, bool nibble_order = false);
+// per-row int8 with the clip at a percentile of |v| (K <= kClipMaxK)
+constexpr int64_t kClipMaxKHost = 16384;
+hipError_t launch_quantize_rows_int8_clip(const void* v, int v_dtype, int64_t R, int64_t K, float pct, int8_t* q,
+                                          float* scale, hipStream_t s);
 hipError_t launch_pack_int4_cols(const void* w, int w_dtype, int64_t K, int64_t N, uint8_t* packed,
                                  float* scale, hipStream_t s);
 

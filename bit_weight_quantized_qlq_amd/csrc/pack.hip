@@ -503,6 +503,97 @@ hipError_t launch_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int6
   return hipGetLastError();
 }
 
+// ------------------------------------------- row int8 with a percentile clip
+// quantize_weight_int8 with clip_percentile: the row's clip is the given
+// percentile of |w| (NumPy's linear method, every step in fp32: q = p/100,
+// v = (K-1) q, i = floor(v), t = v - i, sorted values a, b at i, i+1, then
+// a + (b-a) t for t < 0.5 else b - (b-a)(1-t); v >= K-1 gives the maximum),
+// a zero clip falls back to the row's maximum, scale = clip/127 (1 if 0), and
+// q = clamp(rint(clamp(w, -clip, clip) / scale), -128, 127).
+// One block per row: |w| sorted in LDS by a bitonic network over P2 (the
+// next power of two >= K) slots, the tail padded with +inf.
+constexpr int kClipThreads = 256;
+constexpr int kClipMaxK = 16384;  // 64 KiB of LDS
+template <typename T>
+__global__ void __launch_bounds__(kClipThreads)
+quantize_rows_int8_clip_kernel(const T* __restrict__ v, int K, int P2, float pct, int8_t* __restrict__ q,
+                               float* __restrict__ scale) {
+  extern __shared__ float srt[];
+  __shared__ float clip_s;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const T* vr = v + row * K;
+  for (int i = tid; i < P2; i += kClipThreads)
+    srt[i] = i < K ? fabsf(Elem<T>::load(vr, i)) : __builtin_inff();
+  __syncthreads();
+  for (int k = 2; k <= P2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int pi = tid; pi < P2 / 2; pi += kClipThreads) {
+        const int i = ((pi & ~(j - 1)) << 1) | (pi & (j - 1));  // lower slot of the pair
+        const int l = i | j;
+        const float a = srt[i], b = srt[l];
+        if ((a > b) == ((i & k) == 0)) {
+          srt[i] = b;
+          srt[l] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid == 0) {
+    const float qf = __fdiv_rn(pct, 100.0f);
+    const float vi = __fmul_rn((float)(K - 1), qf);
+    float c;
+    if (vi >= (float)(K - 1)) {
+      c = srt[K - 1];
+    } else {
+      const int i = (int)floorf(vi);
+      const float t = __fsub_rn(vi, (float)i);
+      const float a = srt[i], b = srt[i + 1];
+      const float d = __fsub_rn(b, a);
+      c = t >= 0.5f ? __fsub_rn(b, __fmul_rn(d, __fsub_rn(1.0f, t))) : __fadd_rn(a, __fmul_rn(d, t));
+    }
+    if (c == 0.0f) c = srt[K - 1];
+    clip_s = c;
+    float sc = __fdiv_rn(c, 127.0f);
+    if (sc == 0.0f) sc = 1.0f;
+    scale[row] = sc;
+  }
+  __syncthreads();
+  const float c = clip_s;
+  float sc = __fdiv_rn(c, 127.0f);
+  if (sc == 0.0f) sc = 1.0f;
+  const RowDivider dv(sc);
+  for (int i = tid; i < K; i += kClipThreads) {
+    const float x = fminf(fmaxf(Elem<T>::load(vr, i), -c), c);
+    const float r = fminf(fmaxf(rintf(dv.div(x)), -128.0f), 127.0f);
+    q[row * K + i] = (int8_t)(int32_t)r;
+  }
+}
+
+hipError_t launch_quantize_rows_int8_clip(const void* v, int v_dtype, int64_t R, int64_t K, float pct, int8_t* q,
+                                          float* scale, hipStream_t s) {
+  int P2 = 1;
+  while (P2 < K) P2 <<= 1;
+  const dim3 grid((unsigned)R), block(kClipThreads);
+  const size_t lds = (size_t)P2 * sizeof(float);
+  switch (v_dtype) {
+    case F32:
+      hipLaunchKernelGGL(quantize_rows_int8_clip_kernel<float>, grid, block, lds, s, (const float*)v, (int)K, P2,
+                         pct, q, scale);
+      break;
+    case BF16:
+      hipLaunchKernelGGL(quantize_rows_int8_clip_kernel<bf16_t>, grid, block, lds, s, (const bf16_t*)v, (int)K,
+                         P2, pct, q, scale);
+      break;
+    default:
+      hipLaunchKernelGGL(quantize_rows_int8_clip_kernel<f16_t>, grid, block, lds, s, (const f16_t*)v, (int)K, P2,
+                         pct, q, scale);
+      break;
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------ per-column int4 packing
 // w [K, N] (row-major, N contiguous) -> packed [K/2, N] uint8 with the even k
 // in the high nibble, and scale [N] fp32: s = absmax of the column / 7 (1 if

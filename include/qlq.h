@@ -200,6 +200,20 @@ QLQ_API int qlq_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_
                                    int8_t* q, float* scale, void* stream);
 
 /*
+ * qlq_quantize_rows_int8_clip - quantize_weight_int8 with clip_percentile:
+ * per row, clip = the clip_percentile-th percentile of |v[r, :]| (NumPy's
+ * linear method, every step in fp32: q = p/100, index (K-1) q, the sorted
+ * neighbours a, b and weight t combined as a + (b-a) t for t < 0.5, else
+ * b - (b-a)(1-t)); a zero clip becomes max |v[r, :]|; s = clip/127 (1 if 0);
+ * q = clamp(rint(clamp(v, -clip, clip) / s), -128, 127).  v of v_dtype (F32,
+ * F16 or BF16); q [R, K] int8 and scale [R] fp32 (out).  1 <= K <= 16384
+ * (each row is sorted on chip), 0 <= clip_percentile <= 100.  Non-finite
+ * values give unspecified output.
+ */
+QLQ_API int qlq_quantize_rows_int8_clip(const void* v, int v_dtype, int64_t R, int64_t K,
+                                        float clip_percentile, int8_t* q, float* scale, void* stream);
+
+/*
  * qlq_int8_matmul_int32 - c = a . b^T exactly: a [M, K] int8, b [N, K] int8
  * (the transposed weight layout of int8_matmul_int32), c [M, N] int32 (out).
  * K % 16 == 0 and K <= 131071 (so |c| <= 128*128*K < 2^31).

@@ -248,3 +248,17 @@ def test_w4a8_workspace_and_empty_batch():
     assert L.w4a8_workspace_size(1, 4096, 4096) >= 32 * 4096 * 4 + 4
     assert L.w4a8_workspace_size(8, 4096, 64) >= L.w8a8_workspace_size(8, 4096)
     assert L.w4a8_linear_forward(A, qlq.QLQ_F16, 0, 64, B, A, 32, None, A, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, qlq.QLQ_F32, 4, 64, 99.9, A, B, None), qlq.QLQ_ERR_INVALID_ARG),
+    ((A, qlq.QLQ_F32, 4, 0, 99.9, A, B, None), qlq.QLQ_ERR_INVALID_ARG),
+    ((A, qlq.QLQ_F32, 4, 16385, 99.9, A, B, None), qlq.QLQ_ERR_UNSUPPORTED),   # rows sorted on chip
+    ((A, qlq.QLQ_F32, 4, 64, 100.5, A, B, None), qlq.QLQ_ERR_INVALID_ARG),
+    ((A, qlq.QLQ_F32, 4, 64, -1.0, A, B, None), qlq.QLQ_ERR_INVALID_ARG),
+    ((A, qlq.QLQ_F32, 4, 64, float("nan"), A, B, None), qlq.QLQ_ERR_INVALID_ARG),
+    ((A, 9, 4, 64, 99.9, A, B, None), qlq.QLQ_ERR_UNSUPPORTED),
+    ((ODD, qlq.QLQ_F32, 4, 64, 99.9, A, B, None), qlq.QLQ_ERR_ALIGNMENT),
+])
+def test_clip_quantizer_validation(args, code):
+    assert qlq.lib().qlq_quantize_rows_int8_clip(*args) == code
