@@ -8,17 +8,17 @@
 // The prior-art Metal kernel re-reads every packed row once per batch row and
 // accumulates on the vector ALU.  Here each packed byte is read once for all
 // batch rows and the contraction runs on the matrix cores:
-//  * one block (16 waves) owns 16 packed rows = 64 output rows (4 fields);
-//    the waves split K, issue all their loads before computing, and an
-//    LDS reduction joins their partial sums;
-//  * per 32-k step a lane loads 8 bytes (packed row l%16, 8 consecutive k) and
-//    turns field j of each 4-byte dword into two 16-bit float pairs with one
-//    shift and one and-or:  ((d >> 2j) & 0x00030003) | MAGIC = (OFF + c_k,
-//    OFF + c_k+2)  (OFF = 128 for bf16, 1024 for f16, exact), giving the B
-//    operand of one MFMA 16x16x32 per field; the four fields share one A
-//    operand (x, rows padded to 16 with zeros, k permuted to match);
-//  * sum x*(OFF + c) - (OFF + 1) * sum x = sum x*(c - 1); products are exact
-//    and accumulate in fp32.
+//  * one block (4 waves) owns 8 packed rows = 32 output rows (4 fields);
+//    the waves split K, issue their loads before computing, and an LDS
+//    reduction joins their partial sums;
+//  * a field's 2-bit codes become 16-bit floats in place: masking bits
+//    2f, 2f+1 of a dword shifted by 4t and or-ing MAGIC gives the pair
+//    (OFF + 4^f c_k, OFF + 4^f c_k+2) exactly (OFF = 128 for bf16, 1024 for
+//    f16), the B operand of an MFMA 16x16x32; x is the A operand (16 rows,
+//    k permuted to match);
+//  * sum x*(OFF + 4^f c) = OFF sum x + 4^f sum x*c, so
+//    sum x*(c - 1) = (P - OFF X) / 4^f - X; products are exact and
+//    accumulate in fp32.
 // fp32 x takes a plain vector-ALU kernel.
 #include "common.hpp"
 #include "launch.hpp"
@@ -26,11 +26,10 @@
 namespace qlq {
 
 namespace tern {
-constexpr int ROWS = 16;     // packed rows per block
-constexpr int WAVES = 16;    // waves per block; they split K
-constexpr int THREADS = 64 * WAVES;
-constexpr int KS = 32;       // MFMA k-step
-constexpr int BATCH = 8;     // k-steps a wave loads before computing
+constexpr int ROWS = 8;      // packed rows per block (32 outputs)
+constexpr int WAVES = 4;     // waves per block; they split K
+constexpr int KW = 128;      // k window: a lane loads 32 consecutive k of it
+constexpr int NB = 5;        // windows a wave loads before computing
 }  // namespace tern
 
 template <typename XT> struct TernT;
@@ -61,64 +60,91 @@ template <> struct TernT<f16_t> {
   }
 };
 
-// One block: 16 packed rows x 16 rows of x.  Wave w takes k-steps w, w+16, ...
-// in batches of BATCH: every load of a batch is issued before its MFMAs, so a
-// wave makes one memory round trip per batch (one in total for K <= 4096).
-template <typename XT>
-__global__ void __launch_bounds__(tern::THREADS)
+// One block: 8 packed rows x 16 rows of x; its waves split K in windows of
+// 128 k.
+//  * MFMA column n (= lane % 16) is packed row n % 8; MFMA t covers field
+//    2t + n / 8 of it, so two MFMAs per k-step cover the 4 fields.  The
+//    field's two code bits are masked where they sit, after a shift by 4t
+//    shared by the lanes: (w >> 4t) & (0x00030003 << 2f) | MAGIC is the pair
+//    (OFF + 4^f c, OFF + 4^f c') with f = n / 8, exact; the epilogue divides
+//    by 4^f.
+//  * In a window, lane group q (= lane / 16) owns the 32 consecutive k
+//    32q .. 32q + 31 of its packed row (32 bytes, two 16-byte loads) and of
+//    its x row (64 bytes, four loads), so one wave reads whole 128-byte
+//    lines; MFMA k-step s (0..3) of the window takes k = 32q + 8s .. + 7 from
+//    lane group q for both operands (the same k reach A and B, in an order
+//    the sum does not see).
+//  * A wave issues the loads of NB windows (indexes clamped, no branch), then
+//    computes them in issue order with no branch, so each window waits only
+//    for its own loads.  MASK: K is not a multiple of 128 or the windows do
+//    not split evenly; a lane's k past K (or a window past the end) then
+//    reads zeros for x.  Rows of x past M are left as they are: their outputs
+//    are never stored.
+template <typename XT, bool MASK>
+__global__ void __launch_bounds__(64 * tern::WAVES)
 ternary_mfma_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __restrict__ packed,
                     int R, const XT* __restrict__ wscale, int invert,
                     const XT* __restrict__ bias, XT* __restrict__ y) {
   using namespace tern;
   using TT = TernT<XT>;
-  __shared__ float red[WAVES][4][4][64];  // [wave][field][elem][lane]
+  __shared__ float red[WAVES][2][4][64];  // [wave][mfma][elem][lane]
   __shared__ float xsum_sh[WAVES][16];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r0 = blockIdx.x * ROWS;
   const int m0 = blockIdx.y * 16;
   const int N = 4 * R;
-  const int prow = min(r0 + (lane & 15), R - 1);
-  const int mrow = m0 + (lane & 15);
-  const bool mvalid = mrow < M;
-  const int kofs = (lane >> 4) * 8;
-  const uint8_t* wp = packed + (int64_t)prow * K + kofs;
-  const XT* xp = x + (int64_t)(mvalid ? mrow : 0) * K + kofs;
+  const int n = lane & 15;
+  const int prow = min(r0 + (n & 7), R - 1);
+  const uint32_t fmask = 0x00030003u << (2 * (n >> 3));
+  const int mrow = min(m0 + n, M - 1);
+  const int q = lane >> 4;
+  const uint8_t* wrow = packed + (int64_t)prow * K;
+  const XT* xrow = x + (int64_t)mrow * K;
 
-  f32x4_v P[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) P[j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  f32x4_v P[2];
+  P[0] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  P[1] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   float xs = 0.0f;
 
-  const int nsteps = K / KS;
-  for (int base = wid; base < nsteps; base += WAVES * BATCH) {
-    uint2 wb[BATCH];
-    u32x4_v xv[BATCH];
+  const int nwin = (K + KW - 1) / KW;
+  for (int base = wid; base < nwin; base += WAVES * NB) {
+    uint4 wb[NB][2];
+    u32x4_v xv[NB][4];
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int st = min(base + b * WAVES, nsteps - 1);  // clamped: extra steps are dropped below
-      wb[b] = *reinterpret_cast<const uint2*>(wp + st * KS);
-      xv[b] = *reinterpret_cast<const u32x4_v*>(xp + st * KS);
+    for (int b = 0; b < NB; ++b) {
+      const int win = min(base + b * WAVES, nwin - 1);
+      const int kc = min(win * KW + 32 * q, K - 32);
+      wb[b][0] = *reinterpret_cast<const uint4*>(wrow + kc);
+      wb[b][1] = *reinterpret_cast<const uint4*>(wrow + kc + 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv[b][j] = *reinterpret_cast<const u32x4_v*>(xrow + kc + 8 * j);
     }
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      if (base + b * WAVES >= nsteps) break;
-      const u32x4_v v = mvalid ? xv[b] : u32x4_v{0, 0, 0, 0};
-      // x pairs in the code order of a dword: (k0,k2), (k1,k3) per 4 k
-      u32x4_v a;
-      a[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
-      a[1] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
-      a[2] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
-      a[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
-      xs = TT::dot2(v[3], TT::ONES, TT::dot2(v[2], TT::ONES, TT::dot2(v[1], TT::ONES, TT::dot2(v[0], TT::ONES, xs))));
+    for (int b = 0; b < NB; ++b) {
+      // K % 32 == 0: a lane's 32 k of the window are all inside K or all past it
+      const bool use = !MASK || (base + b * WAVES < nwin && (base + b * WAVES) * KW + 32 * q < K);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4_v bq;
-        bq[0] = ((wb[b].x >> (2 * j)) & 0x00030003u) | TT::MAGIC;
-        bq[1] = ((wb[b].x >> (2 * j + 8)) & 0x00030003u) | TT::MAGIC;
-        bq[2] = ((wb[b].y >> (2 * j)) & 0x00030003u) | TT::MAGIC;
-        bq[3] = ((wb[b].y >> (2 * j + 8)) & 0x00030003u) | TT::MAGIC;
-        P[j] = TT::mma(a, bq, P[j]);
+      for (int st = 0; st < 4; ++st) {
+        const u32x4_v v = use ? xv[b][st] : u32x4_v{0, 0, 0, 0};
+        // x pairs in the code order of a dword: (k0,k2), (k1,k3) per 4 k
+        u32x4_v a;
+        a[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
+        a[1] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
+        a[2] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
+        a[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
+        xs = TT::dot2(v[3], TT::ONES, TT::dot2(v[2], TT::ONES, TT::dot2(v[1], TT::ONES, TT::dot2(v[0], TT::ONES, xs))));
+        const uint4 h = wb[b][st >> 1];
+        const uint32_t w0 = (st & 1) ? h.z : h.x, w1 = (st & 1) ? h.w : h.y;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4_v bq;
+          bq[0] = ((w0 >> (4 * t)) & fmask) | TT::MAGIC;
+          bq[1] = ((w0 >> (4 * t + 8)) & fmask) | TT::MAGIC;
+          bq[2] = ((w1 >> (4 * t)) & fmask) | TT::MAGIC;
+          bq[3] = ((w1 >> (4 * t + 8)) & fmask) | TT::MAGIC;
+          P[t] = TT::mma(a, bq, P[t]);
+        }
       }
     }
   }
@@ -126,31 +152,34 @@ ternary_mfma_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __res
   xs += __shfl_xor(xs, 16, kWave);
   xs += __shfl_xor(xs, 32, kWave);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[wid][j][e][lane] = P[j][e];
+    for (int e = 0; e < 4; ++e) red[wid][t][e][lane] = P[t][e];
   if (lane < 16) xsum_sh[wid][lane] = xs;
   __syncthreads();
 
   const float ws = Elem<XT>::load(wscale, 0);
   const float sigma = invert ? __fdiv_rn(1.0f, ws) : ws;
-  // block outputs: 16 m x 4 fields x 16 packed rows = 1024, one per thread
-  for (int o = tid; o < 1024; o += THREADS) {
-    const int ri = o & 15, mi = (o >> 4) & 15, j = o >> 8;
-    // D layout: lane = (mi / 4) * 16 + ri holds row mi at element mi % 4
-    const int src_lane = (mi >> 2) * 16 + ri, e = mi & 3;
+  // block outputs: 16 m x 4 fields x 8 packed rows = 512
+  for (int o = tid; o < 512; o += 64 * WAVES) {
+    const int ri = o & 7, mi = (o >> 3) & 15, j = o >> 7;
+    // D layout: lane (mi / 4) * 16 + column holds row mi at element mi % 4;
+    // field j is MFMA j / 2, column ri + 8 (j % 2), scaled by 4^(j % 2)
+    const int t = j >> 1, src_lane = (mi >> 2) * 16 + ri + 8 * (j & 1), e = mi & 3;
     float p = 0.0f, X = 0.0f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
-      p += red[w][j][e][src_lane];
+      p += red[w][t][e][src_lane];
       X += xsum_sh[w][mi];
     }
     const int m = m0 + mi, r = r0 + ri;
     if (m < M && r < R) {
-      const int n = r + j * R;
-      float v = sigma * __fmaf_rn(-(TT::OFF + 1.0f), X, p);
-      if (bias) v = v + Elem<XT>::load(bias, n);
-      Elem<XT>::store(y, (int64_t)m * N + n, v);
+      const int nn = r + j * R;
+      // sum x (c - 1) = (P - OFF X) / 4^f - X
+      const float c = __fmaf_rn(-TT::OFF, X, p) * ((j & 1) ? 0.25f : 1.0f);
+      float v = sigma * (c - X);
+      if (bias) v = v + Elem<XT>::load(bias, nn);
+      Elem<XT>::store(y, (int64_t)m * N + nn, v);
     }
   }
 }
@@ -195,14 +224,20 @@ hipError_t launch_ternary_forward(const void* x, int x_dtype, int64_t M, int64_t
                        (const float*)weight_scale, invert, (const float*)bias, (float*)y);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)cdiv(R, tern::ROWS), (unsigned)cdiv(M, 16)), block(tern::THREADS);
+  using namespace tern;
+  dim3 grid((unsigned)cdiv(R, ROWS), (unsigned)cdiv(M, 16)), block(64 * WAVES);
   const int m = (int)M, k = (int)K, r = (int)R;
-  if (x_dtype == BF16)
-    hipLaunchKernelGGL(ternary_mfma_kernel<bf16_t>, grid, block, 0, s, (const bf16_t*)x, m, k, packed, r,
-                       (const bf16_t*)weight_scale, invert, (const bf16_t*)bias, (bf16_t*)y);
-  else
-    hipLaunchKernelGGL(ternary_mfma_kernel<f16_t>, grid, block, 0, s, (const f16_t*)x, m, k, packed, r,
-                       (const f16_t*)weight_scale, invert, (const f16_t*)bias, (f16_t*)y);
+  const int64_t nwin = cdiv(K, KW);
+  const bool mask = K % KW != 0 || nwin % (WAVES * NB) != 0;
+#define QLQ_TERN(XT_, MASK_)                                                                               \
+  hipLaunchKernelGGL((ternary_mfma_kernel<XT_, MASK_>), grid, block, 0, s, (const XT_*)x, m, k, packed, r, \
+                     (const XT_*)weight_scale, invert, (const XT_*)bias, (XT_*)y)
+  if (x_dtype == BF16) {
+    if (mask) QLQ_TERN(bf16_t, true); else QLQ_TERN(bf16_t, false);
+  } else {
+    if (mask) QLQ_TERN(f16_t, true); else QLQ_TERN(f16_t, false);
+  }
+#undef QLQ_TERN
   return hipGetLastError();
 }
 

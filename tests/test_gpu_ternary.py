@@ -103,3 +103,13 @@ def test_identities():
     y_ref, D = oracle.ternary_forward(f32(x), oracle.ternary_pack(zero_t), N, 0.25, bias=f32(bias))
     assert np.array_equal(y_ref, np.broadcast_to(f32(bias), (3, N)))
     assert_close(y, y_ref, D, K, torch.bfloat16, label="ternary zero weights")
+
+
+@pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("M,K,N", [(3, 5120, 4 * 37), (17, 2560, 4 * 21), (8, 2560, 4 * 1728)])
+def test_forward_unmasked_windows(xdt, M, K, N):
+    # K a multiple of 128 whose 128-k windows split evenly over the waves:
+    # the kernel variant with no masking; ragged packed rows and x rows
+    inp = workloads.ternary_inputs(M, K, N, x_dtype=ODT[xdt], weight_scale=0.05, bias=True, seed=M + K)
+    y, y_ref, D = _case(inp, N)
+    assert_close(y, y_ref, D, K, xdt, label=f"ternary unmasked {xdt} {(M, K, N)}")
