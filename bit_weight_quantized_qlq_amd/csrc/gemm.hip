@@ -311,7 +311,10 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
       // the second one when a sub-block spans two groups (else the first again)
       const int u = o - C::B_LOADS;
       const int gd = ((u * 64) >> lg_g) + (G < 64 ? lane >> 5 : 0);  // group after the iteration's first
-      o_off[t] = (gd * NP + n_blk) * 4 + (lane & 31) * 16;
+      // a lane's 4 columns are clamped to the table's width: columns past N
+      // are never stored, and every address stays inside the table
+      const int c4 = min(n_blk + 4 * (lane & 31), NP - 4);
+      o_off[t] = (gd * NP + c4) * 4;
     }
   }
   const int n_other = C::NO / WV + (wid < C::NO % WV ? 1 : 0);
