@@ -196,7 +196,8 @@ QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
                                const void* scales, const void* biases, int sb_dtype, int64_t N, int bits,
                                int group_size, const void* bias, void* y, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  QLQ_REQUIRE(x && packed && scales && biases && y, QLQ_ERR_INVALID_ARG, "null pointer");
+  // x and y may be NULL for an empty batch (M == 0)
+  QLQ_REQUIRE(((x && y) || M == 0) && packed && scales && biases, QLQ_ERR_INVALID_ARG, "null pointer");
   QLQ_REQUIRE(M >= 0 && M < kMaxDim, QLQ_ERR_INVALID_ARG, "invalid M=%lld", (long long)M);
   if (int st = check_affine_shape(N, K, bits, group_size)) return st;
   QLQ_REQUIRE(dtype_ok(x_dtype), QLQ_ERR_UNSUPPORTED, "x_dtype %d", x_dtype);
@@ -262,7 +263,7 @@ QLQ_API int bitlinear_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* packe
 QLQ_API int bitlinear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
                               int64_t N, const void* weight_scale, int invert_weight_scale, const void* bias,
                               void* y, void* stream) {
-  QLQ_REQUIRE(x && packed && weight_scale && y, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(((x && y) || M == 0) && packed && weight_scale, QLQ_ERR_INVALID_ARG, "null pointer");
   QLQ_REQUIRE(M >= 0 && M < kMaxDim && N >= 4 && N < kMaxDim && K >= 1 && K < kMaxDim, QLQ_ERR_INVALID_ARG,
               "invalid shape");
   QLQ_REQUIRE(N % 4 == 0, QLQ_ERR_INVALID_ARG, "N=%lld is not a multiple of 4", (long long)N);
@@ -283,7 +284,7 @@ QLQ_API int bitlinear_forward(const void* x, int x_dtype, int64_t M, int64_t K, 
 // ------------------------------------------------------------------- W8A8
 QLQ_API int qlq_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_t K, int8_t* q, float* scale,
                                    void* stream) {
-  QLQ_REQUIRE(v && q && scale, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE((v && q && scale) || R == 0, QLQ_ERR_INVALID_ARG, "null pointer");
   QLQ_REQUIRE(R >= 0 && R < kMaxDim && K >= 16 && K < kMaxDim, QLQ_ERR_INVALID_ARG, "invalid shape");
   QLQ_REQUIRE(K % 16 == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
   QLQ_REQUIRE(dtype_ok(v_dtype), QLQ_ERR_UNSUPPORTED, "v_dtype %d", v_dtype);
@@ -296,7 +297,7 @@ QLQ_API int qlq_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_
 
 QLQ_API int qlq_quantize_rows_int8_clip(const void* v, int v_dtype, int64_t R, int64_t K, float clip_percentile,
                                         int8_t* q, float* scale, void* stream) {
-  QLQ_REQUIRE(v && q && scale, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE((v && q && scale) || R == 0, QLQ_ERR_INVALID_ARG, "null pointer");
   QLQ_REQUIRE(R >= 0 && R < kMaxDim && K >= 1, QLQ_ERR_INVALID_ARG, "invalid shape");
   QLQ_REQUIRE(K <= qlq::kClipMaxKHost, QLQ_ERR_UNSUPPORTED, "K=%lld above %lld (rows are sorted on chip)",
               (long long)K, (long long)qlq::kClipMaxKHost);
@@ -313,7 +314,7 @@ QLQ_API int qlq_quantize_rows_int8_clip(const void* v, int v_dtype, int64_t R, i
 
 QLQ_API int qlq_int8_matmul_int32(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K, int32_t* c,
                                   void* stream) {
-  QLQ_REQUIRE(a && b && c, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(((a && c) || M == 0) && b, QLQ_ERR_INVALID_ARG, "null pointer");
   QLQ_REQUIRE(M >= 0 && M < kMaxDim && N >= 1 && N < kMaxDim && K >= 16, QLQ_ERR_INVALID_ARG, "invalid shape");
   QLQ_REQUIRE(K % 16 == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
   QLQ_REQUIRE(K <= 131071, QLQ_ERR_UNSUPPORTED, "K=%lld could overflow int32", (long long)K);
@@ -334,7 +335,7 @@ QLQ_API size_t w8a8_workspace_size(int64_t M, int64_t K) {
 QLQ_API int w8a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* w,
                                 const float* scale_w, int64_t N, const void* bias, void* y, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  QLQ_REQUIRE(x && w && scale_w && y, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(((x && y) || M == 0) && w && scale_w, QLQ_ERR_INVALID_ARG, "null pointer");
   QLQ_REQUIRE(M >= 0 && M < kMaxDim && N >= 1 && N < kMaxDim && K >= 16, QLQ_ERR_INVALID_ARG, "invalid shape");
   QLQ_REQUIRE(K % 16 == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
   QLQ_REQUIRE(K <= 131071, QLQ_ERR_UNSUPPORTED, "K=%lld could overflow int32", (long long)K);
@@ -381,7 +382,7 @@ QLQ_API size_t pergroup_workspace_size(int64_t M, int64_t K) {
 QLQ_API int pergroup_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* w,
                                     const float* scale_w, int64_t N, int group_size, const void* bias, void* y,
                                     void* workspace, size_t workspace_bytes, void* stream) {
-  QLQ_REQUIRE(x && w && scale_w && y, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(((x && y) || M == 0) && w && scale_w, QLQ_ERR_INVALID_ARG, "null pointer");
   QLQ_REQUIRE(M >= 0 && M < kMaxDim && N >= 1 && N < kMaxDim && K >= 1, QLQ_ERR_INVALID_ARG, "invalid shape");
   QLQ_REQUIRE(group_size == 64 || group_size == 128 || group_size == 256, QLQ_ERR_UNSUPPORTED,
               "group_size=%d not built (64, 128, 256)", group_size);
@@ -439,7 +440,7 @@ QLQ_API size_t w4a8_workspace_size(int64_t M, int64_t K, int64_t N) {
 QLQ_API int w4a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed_w,
                                 const float* scale_w, int64_t N, const void* bias, void* y, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  QLQ_REQUIRE(x && packed_w && scale_w && y, QLQ_ERR_INVALID_ARG, "null pointer");
+  QLQ_REQUIRE(((x && y) || M == 0) && packed_w && scale_w, QLQ_ERR_INVALID_ARG, "null pointer");
   QLQ_REQUIRE(M >= 0 && M < kMaxDim && N >= 1 && N < kMaxDim && K >= 16, QLQ_ERR_INVALID_ARG, "invalid shape");
   QLQ_REQUIRE(K % 16 == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
   QLQ_REQUIRE(K <= 131071, QLQ_ERR_UNSUPPORTED, "K=%lld could overflow int32", (long long)K);

@@ -30,6 +30,9 @@
  *  - Argument validation (null pointers, sizes, supported bit widths, group
  *    sizes and dtypes, 16-byte alignment of tensor pointers) happens before
  *    any HIP call, so an invalid call has no device side effect.
+ *  - An empty batch (M == 0 rows of x, R == 0 rows to quantize) is a valid
+ *    call that does nothing; the pointers of the empty tensors (x and y, or
+ *    the rows and their outputs) may then be NULL.
  *  - Dtype codes: QLQ_F32, QLQ_F16, QLQ_BF16 (IEEE binary32, binary16, and
  *    bfloat16 = the top half of a binary32).  Narrowing to a storage dtype is
  *    round-to-nearest-even.

@@ -262,3 +262,17 @@ def test_w4a8_workspace_and_empty_batch():
 ])
 def test_clip_quantizer_validation(args, code):
     assert qlq.lib().qlq_quantize_rows_int8_clip(*args) == code
+
+
+def test_empty_batch_accepts_null_row_tensors():
+    L = qlq.lib()
+    assert L.qlq_linear_forward(None, qlq.QLQ_BF16, 0, 256, A, A, A, qlq.QLQ_BF16, 64, 4, 64, None, None,
+                                None, 0, None) == 0
+    assert L.bitlinear_forward(None, qlq.QLQ_BF16, 0, 256, A, 64, A, 0, None, None, None) == 0
+    assert L.w8a8_linear_forward(None, qlq.QLQ_F16, 0, 64, B, A, 32, None, None, None, 0, None) == 0
+    assert L.pergroup_linear_forward(None, qlq.QLQ_F16, 0, 256, A, B, 32, 64, None, None, None, 0, None) == 0
+    assert L.w4a8_linear_forward(None, qlq.QLQ_F16, 0, 64, B, A, 32, None, None, None, 0, None) == 0
+    assert L.qlq_quantize_rows_int8(None, qlq.QLQ_F16, 0, 64, None, None, None) == 0
+    # a non-empty batch still needs them
+    assert L.w8a8_linear_forward(None, qlq.QLQ_F16, 4, 64, B, A, 32, None, A, B, 1 << 20, None) == \
+        qlq.QLQ_ERR_INVALID_ARG
