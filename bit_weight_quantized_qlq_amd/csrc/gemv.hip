@@ -29,7 +29,7 @@
 #include "launch.hpp"
 
 #ifndef QLQ_GEMV_WAVES_PER_BLOCK
-#define QLQ_GEMV_WAVES_PER_BLOCK 8
+#define QLQ_GEMV_WAVES_PER_BLOCK 16
 #endif
 #ifndef QLQ_GEMV_R1
 #define QLQ_GEMV_R1 1  // output rows per wave at M == 1
