@@ -20,7 +20,7 @@
 namespace qlq {
 
 namespace pgmv {
-constexpr int WAVES = 8, THREADS = 64 * WAVES;
+constexpr int WAVES = 16, THREADS = 64 * WAVES;
 constexpr int KMAX = 16384;   // x staged whole in LDS
 constexpr int BATCH = 4;      // chunks a lane loads before computing
 }  // namespace pgmv
