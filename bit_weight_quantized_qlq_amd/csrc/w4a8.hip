@@ -32,7 +32,7 @@ constexpr int NCK = KPS / 8;         // 16-value chunks per block
 constexpr int GPW = NCK / WAVES;     // 8-row groups per wave
 constexpr int MAX_M = 8;
 static_assert(WAVES == 4, "the absmax and partial-sum joins add four waves");
-static_assert(NCK % WAVES == 0 && NCK <= 64, "whole 8-row groups per wave; one thread per chunk and row");
+static_assert(NCK % WAVES == 0 && MAX_M * NCK <= THREADS, "whole 8-row groups per wave; one thread per chunk and row");
 }  // namespace w4s
 
 template <typename XT, int MR, bool BYTES>
