@@ -208,7 +208,7 @@ gemv_pair_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
 }
 
 // ---------------------------------------------------------------------------
-// Latency-bound fast path (16-bit x, 2/4-bit codes, M <= 2, K <= 64*NCH*32).
+// Latency-bound fast path (16-bit x, codes of 1-6 bits, M <= 2, K <= 64*NCH*32).
 //  * x is staged once per block in LDS (one 16-byte load per thread per
 //    2048 bytes of x), so the wave's vector-memory instructions are almost
 //    all weight loads;
@@ -216,8 +216,14 @@ gemv_pair_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
 //    groups when G >= 32*NCH, so a row needs one scale and one bias load per
 //    group the lane touches (group size is a template parameter);
 //  * the x loads are issued first, then every code / scale / bias load of the
-//    wave, then x goes to LDS: one memory round trip per wave.
+//    wave, then x goes to LDS: one memory round trip per wave;
+//  * 1-, 3-, 5- and 6-bit codes: code j and code j + 16 of the chunk's 32 are
+//    taken out of its BITS-word stream at compile-time offsets and joined
+//    into one 16-bit pair, against the x pair (x_j, x_j+16) (at 3, 5 and 6
+//    bits no two codes sit 16 bits apart in one word).
 // ---------------------------------------------------------------------------
+template <int BITS> constexpr bool kStreamPairs = BITS == 1 || BITS == 3 || BITS == 5 || BITS == 6;
+
 template <int BITS, typename XT, int MT, int R, int NCH, int G>
 __global__ void __launch_bounds__(64 * QLQ_GEMV_WAVES_PER_BLOCK)
 gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t* __restrict__ packed,
@@ -226,7 +232,7 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
   using PT = PairTraits<XT>;
   constexpr int CODES = Chunk<BITS>::CODES;          // 32 codes per chunk
   constexpr int WORDS = Chunk<BITS>::WORDS;
-  constexpr int PER = 32 / BITS;                     // codes per word
+  constexpr int PER = kStreamPairs<BITS> ? 1 : 32 / BITS;  // codes per word (2, 4 bits)
   constexpr int XDW = CODES / 2;                     // x dwords per chunk (16)
   constexpr int CPG = G / CODES;                     // chunks per group (1, 2, 4)
   constexpr int NG = NCH >= CPG ? NCH / CPG : 1;     // groups a lane touches
@@ -248,7 +254,7 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
   const int n0 = wave * R;
   const int m0 = blockIdx.y * MT;
   const int cpr = (int)(K / CODES);
-  const int wpr = (int)(K / PER);
+  const int wpr = (int)(K * BITS / 32);
   const int gpr = (int)(K / G);
   const int kx = (int)(K / 8);  // x units per row
 
@@ -291,7 +297,7 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
         p.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
         p.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
         p.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-      } else {  // 2-bit: a word spans two units; permuted after the LDS read
+      } else {  // other widths: pairs span units; permuted after the LDS read
         p = v;
       }
       const float ps = PT::dot2(v.w, PT::ONES, PT::dot2(v.z, PT::ONES, PT::dot2(v.y, PT::ONES, PT::dot2(v.x, PT::ONES, 0.0f))));
@@ -331,6 +337,10 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
       if constexpr (BITS == 4) {
 #pragma unroll
         for (int q = 0; q < XDW; ++q) xp[m][q] = xd[q];
+      } else if constexpr (kStreamPairs<BITS>) {  // pairs (j, j+16) of the chunk's 32 x
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          xp[m][j] = __builtin_amdgcn_perm(xd[8 + j / 2], xd[j / 2], (j & 1) ? 0x07060302u : 0x05040100u);
       } else {  // 2-bit word t covers 8 x dwords: pairs (j, j+8)
 #pragma unroll
         for (int t = 0; t < WORDS; ++t)
@@ -349,14 +359,24 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
       float P[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) P[m] = 0.0f;
+      if constexpr (kStreamPairs<BITS>) {
 #pragma unroll
-      for (int t = 0; t < WORDS; ++t) {
-        const uint32_t w = wv[i][r].w[t];
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t qp =
+              unit_code<BITS>(wv[i][r].w, j) | (unit_code<BITS>(wv[i][r].w, j + 16) << 16) | PT::MAGIC;
 #pragma unroll
-        for (int j = 0; j < PER / 2; ++j) {
-          const uint32_t qp = ((w >> (BITS * j)) & MASK) | PT::MAGIC;
+          for (int m = 0; m < MT; ++m) P[m] = PT::dot2(xp[m][j], qp, P[m]);
+        }
+      } else {
 #pragma unroll
-          for (int m = 0; m < MT; ++m) P[m] = PT::dot2(xp[m][t * (PER / 2) + j], qp, P[m]);
+        for (int t = 0; t < WORDS; ++t) {
+          const uint32_t w = wv[i][r].w[t];
+#pragma unroll
+          for (int j = 0; j < PER / 2; ++j) {
+            const uint32_t qp = ((w >> (BITS * j)) & MASK) | PT::MAGIC;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) P[m] = PT::dot2(xp[m][t * (PER / 2) + j], qp, P[m]);
+          }
         }
       }
 #pragma unroll
@@ -468,8 +488,30 @@ static hipError_t gemv_launch(const void* x, int64_t M, int64_t K, const uint32_
   dim3 grid((unsigned)cdiv(waves, QLQ_GEMV_WAVES_PER_BLOCK), (unsigned)cdiv(M, MT));
   dim3 block(64 * QLQ_GEMV_WAVES_PER_BLOCK);
   constexpr bool pair = (BITS == 2 || BITS == 4) && !std::is_same<XT, float>::value;
-  if constexpr (pair) {
-    const int64_t nch = cdiv(K / Chunk<BITS>::CODES, kWave);
+  constexpr bool flat3 = kStreamPairs<BITS> && !std::is_same<XT, float>::value;
+  const int64_t nch = cdiv(K / Chunk<BITS>::CODES, kWave);
+  if constexpr (flat3) {
+    // 1-, 3-, 5-, 6-bit codes: the flat kernel where it applies, else the generic one
+    if (MT <= 2 && (nch == 1 || nch == 2 || nch == 4)) {
+#define QLQ_FLAT3(NCH_, G_)                                                                                   \
+  hipLaunchKernelGGL((gemv_flat_kernel<BITS, XT, MT, R, NCH_, G_>), grid, block, 0, s, (const XT*)x, M, K,   \
+                     packed, (const XT*)scales, (const XT*)biases, N, (const XT*)bias, (XT*)y)
+#define QLQ_FLAT3_G(NCH_)                 \
+  do {                                    \
+    if (G == 32) QLQ_FLAT3(NCH_, 32);     \
+    else if (G == 64) QLQ_FLAT3(NCH_, 64); \
+    else QLQ_FLAT3(NCH_, 128);            \
+  } while (0)
+      if (nch == 1) QLQ_FLAT3_G(1);
+      else if (nch == 2) QLQ_FLAT3_G(2);
+      else QLQ_FLAT3_G(4);
+#undef QLQ_FLAT3_G
+#undef QLQ_FLAT3
+    } else {
+      hipLaunchKernelGGL((gemv_generic_kernel<BITS, XT, MT, R>), grid, block, 0, s, (const XT*)x, M, K,
+                         packed, (const XT*)scales, (const XT*)biases, N, G, (const XT*)bias, (XT*)y);
+    }
+  } else if constexpr (pair) {
 #define QLQ_FLAT(NCH_, G_)                                                                                    \
   hipLaunchKernelGGL((gemv_flat_kernel<BITS, XT, MT, R, NCH_, G_>), grid, block, 0, s, (const XT*)x, M, K,   \
                      packed, (const XT*)scales, (const XT*)biases, N, (const XT*)bias, (XT*)y)

@@ -143,6 +143,10 @@ SHAPES = [  # (M, K, N, bits, G)
     # path runs them on codes transcoded to bytes
     (1, 416, 200, 3, 32), (3, 640, 77, 5, 128), (9, 448, 130, 6, 64), (17, 384, 129, 1, 128),
     (130, 384, 257, 3, 64), (40, 4160, 72, 5, 64), (33, 640, 131, 6, 128), (20, 448, 250, 1, 32),
+    # M <= 2 with one, two and four 32-code chunks per lane: the flat kernel's
+    # code-stream pairs (j, j+16) at 5, 6 and 1 bits
+    (2, 640, 77, 5, 64), (1, 448, 130, 6, 64), (2, 384, 129, 1, 128), (1, 4096, 96, 6, 128),
+    (2, 8192, 40, 5, 32), (1, 2048, 33, 3, 64),
 ]
 
 
