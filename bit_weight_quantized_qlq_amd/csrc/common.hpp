@@ -54,6 +54,24 @@ template <> struct Elem<f16_t> {
   static __device__ __forceinline__ uint16_t bits(float v) { return __builtin_bit_cast(uint16_t, (f16_t)v); }
 };
 
+// Loads of data that one launch reads once (weight streams): the
+// non-temporal hint streams them through the caches.
+template <typename T> __device__ __forceinline__ T stream_load(const T* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint4 stream_u4(const void* p) {
+  const u32x4_v v = stream_load(reinterpret_cast<const u32x4_v*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// cache-policy operand of the raw buffer loads for the same streams (NT)
+constexpr int kStreamAux = 2;
+template <typename T> __device__ __forceinline__ float stream_elem(const T* p, int64_t i);
+template <> __device__ __forceinline__ float stream_elem<float>(const float* p, int64_t i) { return stream_load(p + i); }
+template <> __device__ __forceinline__ float stream_elem<bf16_t>(const bf16_t* p, int64_t i) {
+  return bf16_to_f32(stream_load(p + i));
+}
+template <> __device__ __forceinline__ float stream_elem<f16_t>(const f16_t* p, int64_t i) {
+  return (float)stream_load(p + i);
+}
+
 // 16-bit storage bits -> fp32 value for a 16-bit storage type.
 template <typename T> __device__ __forceinline__ float bits16_to_f32(uint16_t h);
 template <> __device__ __forceinline__ float bits16_to_f32<bf16_t>(uint16_t h) { return bf16_to_f32(h); }

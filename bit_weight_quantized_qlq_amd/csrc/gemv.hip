@@ -70,19 +70,21 @@ template <int BITS> struct Chunk {
 template <int WORDS> struct WordsT { uint32_t w[WORDS]; };
 
 // a chunk's words; 16- and 8-byte chunks are one load (their offsets are
-// multiples of their size), 3-, 5- and 6-word chunks are dword loads
+// multiples of their size), 3-, 5- and 6-word chunks are dword loads.  Every
+// code word is read once per launch: streaming loads.
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_v;
 template <int WORDS>
 __device__ __forceinline__ WordsT<WORDS> load_words(const uint32_t* p) {
   WordsT<WORDS> r;
   if constexpr (WORDS == 4) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    const u32x4_v v = stream_load(reinterpret_cast<const u32x4_v*>(p));
+    r.w[0] = v[0]; r.w[1] = v[1]; r.w[2] = v[2]; r.w[3] = v[3];
   } else if constexpr (WORDS == 2) {
-    uint2 v = *reinterpret_cast<const uint2*>(p);
-    r.w[0] = v.x; r.w[1] = v.y;
+    const u32x2_v v = stream_load(reinterpret_cast<const u32x2_v*>(p));
+    r.w[0] = v[0]; r.w[1] = v[1];
   } else {
 #pragma unroll
-    for (int i = 0; i < WORDS; ++i) r.w[i] = p[i];
+    for (int i = 0; i < WORDS; ++i) r.w[i] = stream_load(p + i);
   }
   return r;
 }
@@ -126,8 +128,8 @@ gemv_pair_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
     for (int r = 0; r < R; ++r) {
       const int64_t n = (n0 + r < N) ? n0 + r : N - 1;  // clamp: rows past N are computed, not stored
       wv[r] = load_words<WORDS>(packed + n * wpr + c * WORDS);
-      s[r] = Elem<XT>::load(scales, n * gpr + g);
-      b[r] = Elem<XT>::load(biases, n * gpr + g);
+      s[r] = stream_elem<XT>(scales, n * gpr + g);
+      b[r] = stream_elem<XT>(biases, n * gpr + g);
     }
     uint32_t xd[MT][XDW];
 #pragma unroll
@@ -280,8 +282,8 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
       if ((NCH >= CPG && i % CPG == 0) || (NCH < CPG && i == 0)) {
         const int gi = NCH >= CPG ? i / CPG : 0;
         const int g = c / CPG;
-        sr[gi][r] = reinterpret_cast<const uint16_t*>(scales)[(int64_t)n * gpr + g];
-        br[gi][r] = reinterpret_cast<const uint16_t*>(biases)[(int64_t)n * gpr + g];
+        sr[gi][r] = stream_load(reinterpret_cast<const uint16_t*>(scales) + (int64_t)n * gpr + g);
+        br[gi][r] = stream_load(reinterpret_cast<const uint16_t*>(biases) + (int64_t)n * gpr + g);
       }
     }
   }
@@ -436,8 +438,8 @@ gemv_generic_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32
     for (int r = 0; r < R; ++r) {
       const int64_t n = (n0 + r < N) ? n0 + r : N - 1;
       wv[r] = load_words<WORDS>(packed + n * wpr + c * WORDS);
-      s[r] = Elem<XT>::load(scales, n * gpr + g);
-      b[r] = Elem<XT>::load(biases, n * gpr + g);
+      s[r] = stream_elem<XT>(scales, n * gpr + g);
+      b[r] = stream_elem<XT>(biases, n * gpr + g);
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {

@@ -49,19 +49,20 @@ __device__ __forceinline__ u32x4_v unpack16(uint32_t lo, uint32_t hi) {
 // below K2.  Every address stays inside the matrix: otherwise rows past K2
 // repeat the last row (their activations are zero), and columns are clamped
 // by the caller (BYTES = false: col <= ncols - 4) or here (BYTES = true, for
-// N % 4 != 0: each byte's column clamped to ncols - 1).
-template <bool BYTES>
+// N % 4 != 0: each byte's column clamped to ncols - 1).  AUX: the loads'
+// cache-policy operand.
+template <bool BYTES, int AUX = 0>
 __device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, int srow, int vrow, bool full, int K2, int N,
                                       int ncols, int col, uint32_t (&bw)[8]) {
   if constexpr (!BYTES) {
     if (full) {
       const int vo = vrow * N + col;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) bw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, vo, (srow + i) * N, 0);
+      for (int i = 0; i < 8; ++i) bw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, vo, (srow + i) * N, AUX);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        bw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, min(srow + vrow + i, K2 - 1) * N + col, 0, 0);
+        bw[i] = __builtin_amdgcn_raw_buffer_load_b32(r, min(srow + vrow + i, K2 - 1) * N + col, 0, AUX);
     }
   } else {
 #pragma unroll
@@ -70,7 +71,7 @@ __device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, int srow, int vr
       uint32_t v = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, ro + min(col + j, ncols - 1), 0, 0) << (8 * j);
+        v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, ro + min(col + j, ncols - 1), 0, AUX) << (8 * j);
       bw[i] = v;
     }
   }

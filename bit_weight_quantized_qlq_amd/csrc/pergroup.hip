@@ -46,8 +46,8 @@ pergroup_mv_kernel(const XT* __restrict__ x, int K, const int8_t* __restrict__ w
   do {                                                                      \
     _Pragma("unroll") for (int b = 0; b < BATCH; ++b) {                     \
       const int c_ = min((BASE) + 64 * b, nch - 1);                         \
-      wv[b] = *reinterpret_cast<const uint4*>(wr + 16 * c_);                \
-      sc[b] = scale[(int64_t)(16 * c_ / G) * N + nr];                       \
+      wv[b] = stream_u4(wr + 16 * c_); /* read once: streaming loads */   \
+      sc[b] = scale[(int64_t)(16 * c_ / G) * N + nr]; /* lines shared */    \
     }                                                                       \
   } while (0)
   QLQ_MV_LOAD(lane);

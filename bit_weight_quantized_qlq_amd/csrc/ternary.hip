@@ -115,8 +115,8 @@ ternary_mfma_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __res
     for (int b = 0; b < NB; ++b) {
       const int win = min(base + b * WAVES, nwin - 1);
       const int kc = min(win * KW + 32 * q, K - 32);
-      wb[b][0] = *reinterpret_cast<const uint4*>(wrow + kc);
-      wb[b][1] = *reinterpret_cast<const uint4*>(wrow + kc + 16);
+      wb[b][0] = stream_u4(wrow + kc);  // each packed byte is read once: streaming loads
+      wb[b][1] = stream_u4(wrow + kc + 16);
 #pragma unroll
       for (int j = 0; j < 4; ++j) xv[b][j] = *reinterpret_cast<const u32x4_v*>(xrow + kc + 8 * j);
     }

@@ -79,7 +79,7 @@ w4a8_skinny_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __rest
 #pragma unroll
   for (int j = 0; j < GPW; ++j) {
     const int srow = kp0 + 8 * (wid + WAVES * j);
-    if (srow < K2) int4::load8<BYTES>(rb, srow, 0, srow + 8 <= K2, K2, N, N, lcol, bw[j]);
+    if (srow < K2) int4::load8<BYTES, kStreamAux>(rb, srow, 0, srow + 8 <= K2, K2, N, N, lcol, bw[j]);
   }
 
   // quant_a: s = absmax / 127 (1 if 0) per row
