@@ -88,6 +88,22 @@ __device__ __forceinline__ WordsT<WORDS> load_words(const uint32_t* p) {
   }
   return r;
 }
+// the same through a buffer descriptor of one row (offset in bytes, 32-bit)
+template <int WORDS>
+__device__ __forceinline__ WordsT<WORDS> load_words(__amdgpu_buffer_rsrc_t rw, int off) {
+  WordsT<WORDS> r;
+  if constexpr (WORDS == 4) {
+    const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStreamAux);
+    r.w[0] = v[0]; r.w[1] = v[1]; r.w[2] = v[2]; r.w[3] = v[3];
+  } else if constexpr (WORDS == 2) {
+    const u32x2_v v = __builtin_amdgcn_raw_buffer_load_b64(rw, off, 0, kStreamAux);
+    r.w[0] = v[0]; r.w[1] = v[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) r.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, off + 4 * i, 0, kStreamAux);
+  }
+  return r;
+}
 
 // ---------------------------------------------------------------------------
 // Fast path: 16-bit x, 2- or 4-bit codes.
@@ -252,7 +268,7 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
   __shared__ float xsum[MT][XROW];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = blockIdx.x * QLQ_GEMV_WAVES_PER_BLOCK + (tid >> 6);
+  const int wave = blockIdx.x * QLQ_GEMV_WAVES_PER_BLOCK + __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int n0 = wave * R;
   const int m0 = blockIdx.y * MT;
   const int cpr = (int)(K / CODES);
@@ -278,7 +294,8 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int n = (n0 + r < N) ? n0 + r : (int)N - 1;
-      wv[i][r] = load_words<WORDS>(packed + (int64_t)n * wpr + c * WORDS);
+      // rows are wave-uniform: one descriptor per row, the lane's chunk in the offset
+      wv[i][r] = load_words<WORDS>(make_rsrc(packed + (int64_t)n * wpr, wpr * 4), c * WORDS * 4);
       if ((NCH >= CPG && i % CPG == 0) || (NCH < CPG && i == 0)) {
         const int gi = NCH >= CPG ? i / CPG : 0;
         const int g = c / CPG;
