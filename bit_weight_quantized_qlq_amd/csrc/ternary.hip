@@ -99,7 +99,10 @@ ternary_mfma_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __res
   const uint32_t fmask = 0x00030003u << (2 * (n >> 3));
   const int mrow = min(m0 + n, M - 1);
   const int q = lane >> 4;
-  const uint8_t* wrow = packed + (int64_t)prow * K;
+  // the block's packed rows through one buffer descriptor; this lane's row
+  // in the offset
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(packed + (int64_t)r0 * K, (min(R, r0 + ROWS) - r0) * K);
+  const int wrow = (prow - r0) * K;
   const XT* xrow = x + (int64_t)mrow * K;
 
   f32x4_v P[2];
@@ -115,8 +118,11 @@ ternary_mfma_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __res
     for (int b = 0; b < NB; ++b) {
       const int win = min(base + b * WAVES, nwin - 1);
       const int kc = min(win * KW + 32 * q, K - 32);
-      wb[b][0] = stream_u4(wrow + kc);  // each packed byte is read once: streaming loads
-      wb[b][1] = stream_u4(wrow + kc + 16);
+      // each packed byte is read once: streaming loads
+      const u32x4_v w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, wrow + kc, 0, kStreamAux);
+      const u32x4_v w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, wrow + kc + 16, 0, kStreamAux);
+      wb[b][0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+      wb[b][1] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) xv[b][j] = *reinterpret_cast<const u32x4_v*>(xrow + kc + 8 * j);
     }
