@@ -274,9 +274,9 @@ QLQ_API int bitlinear_forward(const void* x, int x_dtype, int64_t M, int64_t K, 
   QLQ_REQUIRE(aligned(weight_scale, es) && aligned(y, es) && (!bias || aligned(bias, es)),
               QLQ_ERR_ALIGNMENT, "misaligned weight_scale / bias / y");
   QLQ_REQUIRE((M + 15) / 16 <= 65535, QLQ_ERR_UNSUPPORTED, "M too large for one launch");
-  // 16-bit x: a block's 8 packed rows sit behind one 32-bit buffer range
-  QLQ_REQUIRE(x_dtype == QLQ_F32 || K <= ((int64_t)1 << 27), QLQ_ERR_UNSUPPORTED,
-              "K=%lld above 2^27 with 16-bit x", (long long)K);
+  // 16-bit x: a block's 16 x rows (and 8 packed rows) sit behind 32-bit buffer ranges
+  QLQ_REQUIRE(x_dtype == QLQ_F32 || K <= ((int64_t)1 << 26), QLQ_ERR_UNSUPPORTED,
+              "K=%lld above 2^26 with 16-bit x", (long long)K);
   if (M == 0) return ok();
   if (int st = current_device_status()) return st;
   return hip_status(qlq::launch_ternary_forward(x, x_dtype, M, K, packed, N, weight_scale,

@@ -103,7 +103,9 @@ ternary_mfma_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __res
   // in the offset
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(packed + (int64_t)r0 * K, (min(R, r0 + ROWS) - r0) * K);
   const int wrow = (prow - r0) * K;
-  const XT* xrow = x + (int64_t)mrow * K;
+  // the block's 16 x rows through one descriptor as well (cached: every block reads them)
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)m0 * K, (min(M, m0 + 16) - m0) * K * 2);
+  const int xrow = (mrow - m0) * K * 2;
 
   f32x4_v P[2];
   P[0] = f32x4_v{0.f, 0.f, 0.f, 0.f};
@@ -124,7 +126,7 @@ ternary_mfma_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __res
       wb[b][0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
       wb[b][1] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xv[b][j] = *reinterpret_cast<const u32x4_v*>(xrow + kc + 8 * j);
+      for (int j = 0; j < 4; ++j) xv[b][j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xrow + 2 * (kc + 8 * j), 0, 0);
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
