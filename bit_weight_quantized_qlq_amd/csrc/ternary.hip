@@ -78,8 +78,8 @@ template <> struct TernT<f16_t> {
 //    computes them in issue order with no branch, so each window waits only
 //    for its own loads.  MASK: K is not a multiple of 128 or the windows do
 //    not split evenly; a lane's k past K (or a window past the end) then
-//    reads zeros for x.  Rows of x past M are left as they are: their outputs
-//    are never stored.
+//    reads zeros for x.  Rows of x past M read zeros through the buffer
+//    range check (no memory traffic); their outputs are never stored.
 template <typename XT, bool MASK>
 __global__ void __launch_bounds__(64 * tern::WAVES)
 ternary_mfma_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __restrict__ packed,
@@ -97,7 +97,6 @@ ternary_mfma_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __res
   const int n = lane & 15;
   const int prow = min(r0 + (n & 7), R - 1);
   const uint32_t fmask = 0x00030003u << (2 * (n >> 3));
-  const int mrow = min(m0 + n, M - 1);
   const int q = lane >> 4;
   // the block's packed rows through one buffer descriptor; this lane's row
   // in the offset
@@ -105,7 +104,9 @@ ternary_mfma_kernel(const XT* __restrict__ x, int M, int K, const uint8_t* __res
   const int wrow = (prow - r0) * K;
   // the block's 16 x rows through one descriptor as well (cached: every block reads them)
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)m0 * K, (min(M, m0 + 16) - m0) * K * 2);
-  const int xrow = (mrow - m0) * K * 2;
+  // row m0 + n; rows past M lie past the descriptor's range and load zeros
+  // without touching memory
+  const int xrow = n * K * 2;
 
   f32x4_v P[2];
   P[0] = f32x4_v{0.f, 0.f, 0.f, 0.f};
