@@ -103,8 +103,9 @@ __device__ __forceinline__ void column_block(const XT* __restrict__ scales, cons
 // x16[m, k] for one row held by one wave: element k of block b (PER codes)
 // goes to position 2j or 2j+1 of the pair order (j, j + PER/2).  Lanes own
 // groups of 16 consecutive elements, interleaved across the wave (16-byte
-// coalesced loads and stores).  Blocks [0, ceil(M/4)) do rows (4 per block),
-// the remaining blocks do the column exponents.
+// coalesced loads and stores).  Blocks [0, ceil(N/64)) do the column
+// exponents, whose chains of dependent loads start first that way; the
+// remaining blocks do rows (4 per block).
 template <int BITS, typename XT, int EPT>
 __global__ void __launch_bounds__(256)
 gemm_prep_wave_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ scales,
@@ -113,13 +114,13 @@ gemm_prep_wave_kernel(const XT* __restrict__ x, int M, int K, const XT* __restri
   constexpr int PER = 32 / BITS;
   constexpr int HALF = PER / 2;
   constexpr int G16 = EPT / 16;
-  const int row_blocks = (M + 3) / 4;
-  if ((int)blockIdx.x >= row_blocks) {
-    column_block<BITS, XT>(scales, biases, ((int)blockIdx.x - row_blocks) * 64, N, K / G, wexp, sbt);
+  const int col_blocks = (N + 63) / 64;
+  if ((int)blockIdx.x < col_blocks) {
+    column_block<BITS, XT>(scales, biases, (int)blockIdx.x * 64, N, K / G, wexp, sbt);
     return;
   }
   const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int m = ((int)blockIdx.x - col_blocks) * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
   const XT* xr = x + (int64_t)m * K;
   float e[EPT];
