@@ -275,8 +275,8 @@ QLQ_API int bitlinear_forward(const void* x, int x_dtype, int64_t M, int64_t K, 
               QLQ_ERR_ALIGNMENT, "misaligned weight_scale / bias / y");
   QLQ_REQUIRE((M + 15) / 16 <= 65535, QLQ_ERR_UNSUPPORTED, "M too large for one launch");
   // 16-bit x: a block's 16 x rows (and 8 packed rows) sit behind 32-bit buffer ranges
-  QLQ_REQUIRE(x_dtype == QLQ_F32 || K <= ((int64_t)1 << 26), QLQ_ERR_UNSUPPORTED,
-              "K=%lld above 2^26 with 16-bit x", (long long)K);
+  QLQ_REQUIRE(x_dtype == QLQ_F32 || K < ((int64_t)1 << 26), QLQ_ERR_UNSUPPORTED,
+              "K=%lld not below 2^26 with 16-bit x", (long long)K);
   if (M == 0) return ok();
   if (int st = current_device_status()) return st;
   return hip_status(qlq::launch_ternary_forward(x, x_dtype, M, K, packed, N, weight_scale,

@@ -182,7 +182,7 @@ QLQ_API int bitlinear_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* packe
  *   to equal the weight-scale dtype); bias [N] of x_dtype or NULL;
  *   y [M, N] of x_dtype (out), fp32 accumulation, bias added after scaling,
  *   one final rounding.  N % 4 == 0, K % 32 == 0, M >= 1; with 16-bit x
- *   K <= 2^26 (QLQ_ERR_UNSUPPORTED above).
+ *   K < 2^26 (QLQ_ERR_UNSUPPORTED otherwise).
  */
 QLQ_API int bitlinear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
                               const uint8_t* packed, int64_t N, const void* weight_scale,

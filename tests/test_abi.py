@@ -117,7 +117,7 @@ def test_pack_validation(args, code):
     (dict(x_dtype=5), qlq.QLQ_ERR_UNSUPPORTED),
     (dict(x=ODD), qlq.QLQ_ERR_ALIGNMENT),
     (dict(y=A + 1), qlq.QLQ_ERR_ALIGNMENT),
-    (dict(K=(1 << 26) + 32), qlq.QLQ_ERR_UNSUPPORTED),   # 16-bit x: K <= 2^26
+    (dict(K=1 << 26), qlq.QLQ_ERR_UNSUPPORTED),          # 16-bit x: K < 2^26
 ])
 def test_bitlinear_validation(kw, code):
     a = dict(x=A, x_dtype=qlq.QLQ_BF16, M=8, K=64, packed=A, N=16, ws=B, inv=0, bias=None, y=A)
