@@ -81,8 +81,10 @@ int current_device_status() {
   } while (0)
 
 bool affine_bits_ok(int bits) { return (bits >= 1 && bits <= 6) || bits == 8; }
-// widths whose GEMM runs on codes transcoded to the 8-bit layout
-bool transcoded_gemm(int bits) { return bits != 2 && bits != 4 && bits != 8; }
+// the packed width the GEMM runs on: 1- and 3-bit codes are transcoded to
+// the 4-bit layout, 5- and 6-bit codes to the 8-bit one
+int gemm_bits(int bits) { return bits == 1 || bits == 3 ? 4 : bits == 5 || bits == 6 ? 8 : bits; }
+bool transcoded_gemm(int bits) { return gemm_bits(bits) != bits; }
 
 int check_affine_shape(int64_t N, int64_t K, int bits, int G) {
   QLQ_REQUIRE(N >= 1 && K >= 1 && N < kMaxDim && K < kMaxDim, QLQ_ERR_INVALID_ARG,
@@ -188,7 +190,7 @@ QLQ_API size_t qlq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int bi
   if (M <= 0 || K <= 0 || N <= 0 || group_size <= 0 || K % group_size) return 0;
   if (!takes_gemm(M, K, N, group_size, x_dtype)) return 0;
   size_t need = (qlq::affine_gemm_workspace(M, K, N, group_size) + 255) & ~(size_t)255;
-  if (transcoded_gemm(bits)) need += (size_t)N * (size_t)K;  // the codes as bytes (the 8-bit layout)
+  if (transcoded_gemm(bits)) need += (size_t)N * (size_t)K * gemm_bits(bits) / 8;  // the transcoded codes
   return need;
 }
 
@@ -219,14 +221,16 @@ QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
   if (int st = current_device_status()) return st;
   hipStream_t s = (hipStream_t)stream;
   if (gemm && transcoded_gemm(bits)) {
-    // 1, 3, 5, 6 bits: the codes are unpacked to one byte each, which is the
-    // 8-bit packed layout, and the 8-bit GEMM runs on them with the same
-    // scales and biases
-    uint32_t* codes8 = (uint32_t*)((char*)workspace +
-                                   ((qlq::affine_gemm_workspace(M, K, N, group_size) + 255) & ~(size_t)255));
-    if (int st = hip_status(qlq::launch_affine_unpack(packed, N, K, bits, (uint8_t*)codes8, s), "transcode"))
-      return st;
-    return hip_status(qlq::launch_affine_gemm(x, x_dtype, M, K, codes8, scales, biases, N, 8, group_size, bias,
+    // 1, 3, 5, 6 bits: the codes are rewritten in the 4-bit (1, 3) or 8-bit
+    // (5, 6: one byte per code) packed layout, and that width's GEMM runs on
+    // them with the same scales and biases
+    uint32_t* codes = (uint32_t*)((char*)workspace +
+                                  ((qlq::affine_gemm_workspace(M, K, N, group_size) + 255) & ~(size_t)255));
+    const int wb = gemm_bits(bits);
+    const hipError_t e = wb == 4 ? qlq::launch_affine_to_nibbles(packed, N, K, bits, codes, s)
+                                 : qlq::launch_affine_unpack(packed, N, K, bits, (uint8_t*)codes, s);
+    if (int st = hip_status(e, "transcode")) return st;
+    return hip_status(qlq::launch_affine_gemm(x, x_dtype, M, K, codes, scales, biases, N, wb, group_size, bias,
                                               y, workspace, s),
                       "affine gemm");
   }

@@ -14,6 +14,9 @@ hipError_t launch_affine_pack(const float* w, int64_t N, int64_t K, int bits, in
                               int* err_flag, hipStream_t s);
 hipError_t launch_affine_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits,
                                 uint8_t* codes, hipStream_t s);
+// 1- or 3-bit codes rewritten in the 4-bit packed layout (N*K % 32 == 0)
+hipError_t launch_affine_to_nibbles(const uint32_t* packed, int64_t N, int64_t K, int bits,
+                                    uint32_t* out, hipStream_t s);
 hipError_t launch_affine_dequant(const uint32_t* packed, const void* scales, const void* biases,
                                  int sb_dtype, int64_t N, int64_t K, int bits, int G, float* w,
                                  hipStream_t s);

@@ -159,6 +159,43 @@ hipError_t launch_affine_unpack(const uint32_t* packed, int64_t N, int64_t K, in
 #undef QLQ_CALL
 }
 
+// ------------------------------------------------ affine codes to nibbles
+// Codes of at most 4 bits rewritten in the 4-bit packed layout (code k at
+// bits 4 (k mod 8) of word k / 8).  Rows are whole words in both layouts, so
+// the N*K codes are one stream on both sides; a thread takes one unit of 32
+// codes and writes its four words (N*K % 32 == 0).
+template <int BITS>
+__global__ void __launch_bounds__(256)
+affine_to_nibbles_kernel(const uint32_t* __restrict__ packed, int64_t units, uint4* __restrict__ out) {
+  static_assert(BITS <= 4, "codes must fit a nibble");
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= units) return;
+  uint32_t wd[BITS];
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) wd[i] = packed[u * BITS + i];
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[i] |= unit_code<BITS>(wd, 8 * i + j) << (4 * j);
+  }
+  out[u] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_affine_to_nibbles(const uint32_t* packed, int64_t N, int64_t K, int bits,
+                                    uint32_t* out, hipStream_t s) {
+  const int64_t units = N * K / 32;
+  dim3 grid((unsigned)cdiv(units, 256)), block(256);
+  if (bits == 1)
+    hipLaunchKernelGGL(affine_to_nibbles_kernel<1>, grid, block, 0, s, packed, units, (uint4*)out);
+  else if (bits == 3)
+    hipLaunchKernelGGL(affine_to_nibbles_kernel<3>, grid, block, 0, s, packed, units, (uint4*)out);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------- affine dequantize
 // w = fma(scale, q, bias): one rounding of the exact value, in fp32.  One
 // thread per unit of 32 codes (a unit never straddles a group: G % 32 == 0).

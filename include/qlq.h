@@ -116,7 +116,9 @@ QLQ_API int qlq_dequantize(const uint32_t* packed, const void* scales, const voi
  * needs for these arguments (0 when the call takes the skinny path, or the
  * arguments are invalid).  GEMM path: x rescaled to fp16 [M, K], per-row and
  * per-column exponents, and the per-group fp16 (scale, bias) pairs
- * [K/group_size, round_up(N, 4)].
+ * [K/group_size, round_up(N, 4)]; for 1-, 3-, 5- and 6-bit codes also the
+ * codes rewritten for the GEMM (N*K/2 bytes as nibbles for 1 and 3 bits,
+ * N*K bytes for 5 and 6).
  */
 QLQ_API size_t qlq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int bits,
                                          int group_size, int x_dtype);
@@ -141,8 +143,10 @@ QLQ_API size_t qlq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int bi
  * kernel.  Larger M takes the MFMA GEMM when K % 64 == 0, 256*K < 2^31 and
  * 4*(K/group_size)*round_up(N, 4) < 2^31 (its operands are addressed with
  * 32-bit buffer offsets); other shapes take the skinny kernel, and
- * qlq_linear_workspace_size() returns 0 for them.  bits in {2, 4, 8};
- * group_size in {32, 64, 128}; x_dtype == sb_dtype in {F32, F16, BF16}.
+ * qlq_linear_workspace_size() returns 0 for them.  bits in {1, ..., 6, 8}
+ * (the GEMM runs 1- and 3-bit codes as 4-bit ones, 5- and 6-bit codes as
+ * 8-bit ones, transcoded in the workspace); group_size in {32, 64, 128};
+ * x_dtype == sb_dtype in {F32, F16, BF16}.
  */
 QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
                                const uint32_t* packed, const void* scales,

@@ -79,11 +79,13 @@ def test_linear_forward_validation(kw, code):
     assert qlq.last_error() != ""
 
 
-def test_transcoded_widths_need_room_for_byte_codes():
+def test_transcoded_widths_need_room_for_their_codes():
+    # 1- and 3-bit codes are rewritten as nibbles (N*K/2 bytes), 5- and 6-bit
+    # codes as bytes (N*K)
     L = qlq.lib()
     base = L.qlq_linear_workspace_size(2048, 4096, 11008, 4, 128, qlq.QLQ_BF16)
-    for bits in (1, 3, 5, 6):
-        assert L.qlq_linear_workspace_size(2048, 4096, 11008, bits, 128, qlq.QLQ_BF16) >= base + 11008 * 4096
+    for bits, per in ((1, 0.5), (3, 0.5), (5, 1), (6, 1)):
+        assert L.qlq_linear_workspace_size(2048, 4096, 11008, bits, 128, qlq.QLQ_BF16) >= base + 11008 * 4096 * per
     assert L.qlq_linear_workspace_size(4, 4096, 11008, 3, 128, qlq.QLQ_BF16) == 0   # skinny: none
 
 
