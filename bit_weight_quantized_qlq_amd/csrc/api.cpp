@@ -83,7 +83,7 @@ int current_device_status() {
 bool affine_bits_ok(int bits) { return (bits >= 1 && bits <= 6) || bits == 8; }
 // the packed width the GEMM runs on: 1- and 3-bit codes are transcoded to
 // the 4-bit layout, 5- and 6-bit codes to the 8-bit one
-int gemm_bits(int bits) { return bits == 1 || bits == 3 ? 4 : bits == 5 || bits == 6 ? 8 : bits; }
+int gemm_bits(int bits) { return bits <= 3 ? 4 : bits == 5 || bits == 6 ? 8 : bits; }
 bool transcoded_gemm(int bits) { return gemm_bits(bits) != bits; }
 
 int check_affine_shape(int64_t N, int64_t K, int bits, int G) {

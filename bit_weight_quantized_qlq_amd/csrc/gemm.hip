@@ -214,10 +214,12 @@ gemm_prep_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ 
 // lane's codes contiguous:
 //   4-bit: word 4h + s        (8 codes, pairs (j, j+4))        A chunk 4h + s
 //   8-bit: words 8h+2s, +1    (2 x 4 codes, pairs (0,2),(1,3)) A chunk 4h + s
-//   2-bit: word s, pairs 4h..4h+3 of (j, j+8)                 A chunk 2s + h
-// (x16 already holds every word's values in the pair order).
+// (x16 already holds every word's values in the pair order).  1- to 3-bit
+// codes reach this kernel rewritten as 4-bit codes, 5- and 6-bit ones as
+// 8-bit codes.
 namespace gemm {
 template <int BITS, int BK, int STAGES, int WV, int BMT> struct Cfg {
+  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit packed codes");
   static constexpr int KSPLIT = WV / 4;             // waves per sub-tile (k-split)
   static constexpr int MI = BMT / 64;               // MFMA row tiles per wave (wave tile BMT/2 x 64)
   static constexpr int SPW = 4 / KSPLIT;            // k-steps per wave per 64-k sub-block
@@ -341,8 +343,6 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
   // wave's k-steps of a sub-block are s = kh*SPW + sl, sl < SPW.
   // B: the words of those steps are contiguous: NBW words from byte boff
   constexpr int NBW = BITS == 8 ? 2 * SPW : SPW;
-  // SB: 2-bit codes with 32-wide groups change group between steps 1 and 2
-  constexpr bool SB2 = BITS == 2 && SPW == 4;
   constexpr int NBR = NBW == 8 ? 2 : 1;  // 16-byte B reads per fragment
   int aoff[MI][C::U][SPW];
   int boff[2][C::U][NBR];
@@ -355,7 +355,7 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
 #pragma unroll
       for (int sl = 0; sl < SPW; ++sl) {
         const int st = kh * SPW + sl;
-        const int c = 8 * u + (BITS == 2 ? 2 * st + h : 4 * h + st);
+        const int c = 8 * u + 4 * h + st;
         aoff[i][u][sl] = ra * C::A_ROW + (c ^ lds_swz<C::A_CB>(ra)) * 16;
       }
   }
@@ -365,12 +365,12 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
 #pragma unroll
     for (int u = 0; u < C::U; ++u) {
       // first word of this wave's steps within the row's sub-block
-      const int w0 = BITS == 4 ? 4 * h + kh * SPW : BITS == 2 ? kh * SPW : 8 * h + 2 * kh * SPW;
+      const int w0 = BITS == 4 ? 4 * h + kh * SPW : 8 * h + 2 * kh * SPW;
       const int cb = (C::RB / C::U / 16) * u + w0 / 4;  // chunk (4 words per chunk)
 #pragma unroll
       for (int q = 0; q < NBR; ++q)
         boff[i][u][q] = C::B_BASE + rb * C::RB + ((cb + q) ^ lds_swz<C::B_CB>(rb)) * 16 + (w0 % 4) * 4;
-      const int gi = G < 64 ? (BITS == 2 ? kh : h) : 0;
+      const int gi = G < 64 ? h : 0;
       soff[i][u] = C::SB_BASE + u * 1024 + gi * 512 + rb * 4;
     }
   }
@@ -393,11 +393,7 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
               af[i][sl] = *reinterpret_cast<const u32x4_v*>(sa_ + aoff[i][u][sl]);                 \
       u32x4_v bq[2][SPW]; /* [j][sl]: dequantized B operands */                                    \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                              \
-        uint32_t e[2];                                                                             \
-        e[0] = *reinterpret_cast<const uint32_t*>(ss_ + soff[j][u]);                               \
-        e[1] = e[0];                                                                               \
-        if constexpr (SB2)                                                                         \
-          if (G < 64) e[1] = *reinterpret_cast<const uint32_t*>(ss_ + soff[j][u] + 512);           \
+        const uint32_t ee = *reinterpret_cast<const uint32_t*>(ss_ + soff[j][u]);                 \
         uint32_t w[NBW];                                                                           \
         if constexpr (NBW == 2) {                                                                  \
           const uint2 v = *reinterpret_cast<const uint2*>(sb_ + boff[j][u][0]);                    \
@@ -409,13 +405,11 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
           }                                                                                        \
         }                                                                                          \
         _Pragma("unroll") for (int sl = 0; sl < SPW; ++sl) {                                       \
-          const uint32_t ee = SB2 && sl >= 2 ? e[1] : e[0];                                        \
           const f16x2_v s2 = __builtin_bit_cast(f16x2_v, (ee & 0xFFFFu) * 0x10001u);               \
           const f16x2_v b2 = __builtin_bit_cast(f16x2_v, (ee >> 16) * 0x10001u);                   \
           _Pragma("unroll") for (int p = 0; p < 4; ++p) {                                          \
             uint32_t qd;                                                                           \
             if constexpr (BITS == 4) qd = (w[sl] >> (4 * p)) & MASK;                               \
-            else if constexpr (BITS == 2) qd = (w[sl] >> (2 * (4 * h + p))) & MASK;                \
             else qd = (w[2 * sl + (p >> 1)] >> (8 * (p & 1))) & MASK;                              \
             bq[j][sl][p] = __builtin_bit_cast(                                                     \
                 uint32_t, __builtin_elementwise_fma(s2, __builtin_bit_cast(f16x2_v, qd), b2));     \
@@ -553,8 +547,7 @@ static hipError_t gemm_launch(const void* x, int64_t M, int64_t K, const uint32_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 4-bit codes only: an 8-bit 256-row stage does not fit twice in a compute
-  // unit's LDS, and the 2-bit decode of a 128x64 wave tile runs out of
-  // registers
+  // unit's LDS
   const int64_t tall_tiles = cdiv(M, gemm::TILE_M_TALL) * cdiv(N, gemm::BN);
   const bool tall = BITS == 4 && tall_tiles >= 2 * 256;
   const int64_t tiles = tall ? tall_tiles : cdiv(M, gemm::TILE_M) * cdiv(N, gemm::BN);
@@ -580,11 +573,10 @@ hipError_t launch_affine_gemm(const void* x, int x_dtype, int64_t M, int64_t K,
                               const uint32_t* packed, const void* scales, const void* biases,
                               int64_t N, int bits, int G, const void* bias, void* y,
                               void* workspace, hipStream_t s) {
-  switch (bits) {
-    case 2: return gemm_dispatch_x<2>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, workspace, s);
-    case 4: return gemm_dispatch_x<4>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, workspace, s);
-    default: return gemm_dispatch_x<8>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, workspace, s);
-  }
+  // 4- or 8-bit packed codes (the caller transcodes the other widths)
+  if (bits == 4) return gemm_dispatch_x<4>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, workspace, s);
+  if (bits == 8) return gemm_dispatch_x<8>(x, x_dtype, M, K, packed, scales, biases, N, G, bias, y, workspace, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace qlq

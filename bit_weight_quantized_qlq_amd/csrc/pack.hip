@@ -189,6 +189,8 @@ hipError_t launch_affine_to_nibbles(const uint32_t* packed, int64_t N, int64_t K
   dim3 grid((unsigned)cdiv(units, 256)), block(256);
   if (bits == 1)
     hipLaunchKernelGGL(affine_to_nibbles_kernel<1>, grid, block, 0, s, packed, units, (uint4*)out);
+  else if (bits == 2)
+    hipLaunchKernelGGL(affine_to_nibbles_kernel<2>, grid, block, 0, s, packed, units, (uint4*)out);
   else if (bits == 3)
     hipLaunchKernelGGL(affine_to_nibbles_kernel<3>, grid, block, 0, s, packed, units, (uint4*)out);
   else
