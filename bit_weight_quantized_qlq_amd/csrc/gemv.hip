@@ -335,41 +335,57 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
 
+  // every x chunk of this lane out of LDS first, before anything waits for
+  // the weights, so the LDS latency overlaps the HBM latency; no branch, so
+  // all of these reads can be issued at once (lanes past the row compute on
+  // the re-read last chunk and drop the result below)
+  float X[NCH][MT];
+  uint32_t xp[NCH][MT][XDW];
+  uint4 xu[NCH][MT][4];
+  float xf[NCH][MT][4];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = lane * NCH + i;
-    if (c >= cpr) break;
-    float X[MT];
-    uint32_t xp[MT][XDW];
+  for (int i = 0; i < NCH; ++i)
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      uint32_t xd[XDW];
-      float xsm = 0.0f;
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int pos = q * (64 * NCH) + i * 64 + lane;
-        const uint4 v = xs[m][pos];
-        xd[4 * q] = v.x; xd[4 * q + 1] = v.y; xd[4 * q + 2] = v.z; xd[4 * q + 3] = v.w;
-        xsm += xsum[m][pos];
+        xu[i][m][q] = xs[m][pos];
+        xf[i][m][q] = xsum[m][pos];
       }
-      X[m] = xsm;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      uint32_t xd[XDW];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = xu[i][m][q];
+        xd[4 * q] = v.x; xd[4 * q + 1] = v.y; xd[4 * q + 2] = v.z; xd[4 * q + 3] = v.w;
+      }
+      X[i][m] = ((xf[i][m][0] + xf[i][m][1]) + xf[i][m][2]) + xf[i][m][3];
       if constexpr (BITS == 4) {
 #pragma unroll
-        for (int q = 0; q < XDW; ++q) xp[m][q] = xd[q];
+        for (int q = 0; q < XDW; ++q) xp[i][m][q] = xd[q];
       } else if constexpr (kStreamPairs<BITS>) {  // pairs (j, j+16) of the chunk's 32 x
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          xp[m][j] = __builtin_amdgcn_perm(xd[8 + j / 2], xd[j / 2], (j & 1) ? 0x07060302u : 0x05040100u);
+          xp[i][m][j] = __builtin_amdgcn_perm(xd[8 + j / 2], xd[j / 2], (j & 1) ? 0x07060302u : 0x05040100u);
       } else {  // 2-bit word t covers 8 x dwords: pairs (j, j+8)
 #pragma unroll
         for (int t = 0; t < WORDS; ++t)
 #pragma unroll
           for (int j = 0; j < PER / 2; ++j)
-            xp[m][t * (PER / 2) + j] = __builtin_amdgcn_perm(xd[t * (PER / 2) + PER / 4 + j / 2],
-                                                             xd[t * (PER / 2) + j / 2],
-                                                             (j & 1) ? 0x07060302u : 0x05040100u);
+            xp[i][m][t * (PER / 2) + j] = __builtin_amdgcn_perm(xd[t * (PER / 2) + PER / 4 + j / 2],
+                                                                xd[t * (PER / 2) + j / 2],
+                                                                (j & 1) ? 0x07060302u : 0x05040100u);
       }
     }
+  }
+
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const bool live = lane * NCH + i < cpr;
     const int gi = NCH >= CPG ? i / CPG : 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -384,7 +400,7 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
           const uint32_t qp =
               unit_code<BITS>(wv[i][r].w, j) | (unit_code<BITS>(wv[i][r].w, j + 16) << 16) | PT::MAGIC;
 #pragma unroll
-          for (int m = 0; m < MT; ++m) P[m] = PT::dot2(xp[m][j], qp, P[m]);
+          for (int m = 0; m < MT; ++m) P[m] = PT::dot2(xp[i][m][j], qp, P[m]);
         }
       } else {
 #pragma unroll
@@ -394,12 +410,15 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
           for (int j = 0; j < PER / 2; ++j) {
             const uint32_t qp = ((w >> (BITS * j)) & MASK) | PT::MAGIC;
 #pragma unroll
-            for (int m = 0; m < MT; ++m) P[m] = PT::dot2(xp[m][t * (PER / 2) + j], qp, P[m]);
+            for (int m = 0; m < MT; ++m) P[m] = PT::dot2(xp[i][m][t * (PER / 2) + j], qp, P[m]);
           }
         }
       }
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m][r] = __fmaf_rn(s, P[m], __fmaf_rn(cb, X[m], acc[m][r]));
+      for (int m = 0; m < MT; ++m) {
+        const float a = __fmaf_rn(s, P[m], __fmaf_rn(cb, X[i][m], acc[m][r]));
+        acc[m][r] = live ? a : acc[m][r];
+      }
     }
   }
 
