@@ -383,6 +383,12 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
     }
   }
 
+  // the code mask held in a vector register the compiler cannot fold, so that
+  // mask-and-or with the exponent pattern is one v_and_or_b32 per pair (a
+  // VALU instruction reads at most one literal or scalar operand here)
+  uint32_t maskv;
+  asm("" : "=v"(maskv) : "0"(MASK));
+  constexpr uint32_t magic = PT::MAGIC;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const bool live = lane * NCH + i < cpr;
@@ -398,7 +404,7 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const uint32_t qp =
-              unit_code<BITS>(wv[i][r].w, j) | (unit_code<BITS>(wv[i][r].w, j + 16) << 16) | PT::MAGIC;
+              unit_code<BITS>(wv[i][r].w, j) | (unit_code<BITS>(wv[i][r].w, j + 16) << 16) | magic;
 #pragma unroll
           for (int m = 0; m < MT; ++m) P[m] = PT::dot2(xp[i][m][j], qp, P[m]);
         }
@@ -408,7 +414,7 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
           const uint32_t w = wv[i][r].w[t];
 #pragma unroll
           for (int j = 0; j < PER / 2; ++j) {
-            const uint32_t qp = ((w >> (BITS * j)) & MASK) | PT::MAGIC;
+            const uint32_t qp = ((w >> (BITS * j)) & maskv) | magic;
 #pragma unroll
             for (int m = 0; m < MT; ++m) P[m] = PT::dot2(xp[i][m][t * (PER / 2) + j], qp, P[m]);
           }
