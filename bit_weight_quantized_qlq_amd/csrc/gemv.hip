@@ -276,13 +276,24 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
   const int gpr = (int)(K / G);
   const int kx = (int)(K / 8);  // x units per row
 
-  // ---- 1. x loads first (they gate the LDS staging)
-  uint4 xr[XU4];
+  // ---- 1. x loads first (they gate the LDS staging).  Code streams pair x_j
+  // with x_j+16 of each 32-value chunk, so staged unit o = 2q + h of a chunk
+  // takes halves h of the chunk's units q and q + 2 (xr and xr2).
+  constexpr bool PAIRS16 = kStreamPairs<BITS>;
+  uint4 xr[XU4], xr2[PAIRS16 ? XU4 : 1];
 #pragma unroll
   for (int i = 0; i < XU4; ++i) {
     const int idx = tid + THREADS * i, m = idx / XROW, u = idx % XROW;
     const int mm = (m0 + m < M) ? m0 + m : (int)M - 1;
-    xr[i] = (m < MT && u < kx) ? reinterpret_cast<const uint4*>(x + (int64_t)mm * K)[u] : make_uint4(0, 0, 0, 0);
+    const uint4* xrow = reinterpret_cast<const uint4*>(x + (int64_t)mm * K);
+    const bool in = m < MT && u < kx;
+    if constexpr (PAIRS16) {
+      const int ua = (u & ~3) + ((u & 3) >> 1);  // unit q of the chunk; q + 2 is two units on
+      xr[i] = in ? xrow[ua] : make_uint4(0, 0, 0, 0);
+      xr2[i] = in ? xrow[ua + 2] : make_uint4(0, 0, 0, 0);
+    } else {
+      xr[i] = in ? xrow[u] : make_uint4(0, 0, 0, 0);
+    }
   }
   // ---- 2. every weight load of this wave, chunk by chunk
   WordsT<WORDS> wv[NCH][R];
@@ -316,10 +327,20 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
         p.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
         p.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
         p.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-      } else {  // other widths: pairs span units; permuted after the LDS read
+      } else if constexpr (PAIRS16) {  // pairs (x_j, x_j+16): half h of units q and q + 2
+        const uint4 v2 = xr2[i];
+        const bool hi = (u & 1) != 0;
+        const uint32_t a0 = hi ? v.z : v.x, a1 = hi ? v.w : v.y;
+        const uint32_t b0 = hi ? v2.z : v2.x, b1 = hi ? v2.w : v2.y;
+        p.x = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+        p.y = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+        p.z = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+        p.w = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+      } else {  // 2-bit codes: pairs (j, j+8) span units; permuted after the LDS read
         p = v;
       }
-      const float ps = PT::dot2(v.w, PT::ONES, PT::dot2(v.z, PT::ONES, PT::dot2(v.y, PT::ONES, PT::dot2(v.x, PT::ONES, 0.0f))));
+      // the staged unit's 8 values (any split of a chunk's 32 works for X)
+      const float ps = PT::dot2(p.w, PT::ONES, PT::dot2(p.z, PT::ONES, PT::dot2(p.y, PT::ONES, PT::dot2(p.x, PT::ONES, 0.0f))));
       const int c = u >> 2, q = u & 3;
       const int pos = q * (64 * NCH) + (c % NCH) * 64 + c / NCH;
       xs[m][pos] = p;
@@ -367,10 +388,9 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
       if constexpr (BITS == 4) {
 #pragma unroll
         for (int q = 0; q < XDW; ++q) xp[i][m][q] = xd[q];
-      } else if constexpr (kStreamPairs<BITS>) {  // pairs (j, j+16) of the chunk's 32 x
+      } else if constexpr (PAIRS16) {  // staged as pairs (j, j+16) already
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          xp[i][m][j] = __builtin_amdgcn_perm(xd[8 + j / 2], xd[j / 2], (j & 1) ? 0x07060302u : 0x05040100u);
+        for (int q = 0; q < XDW; ++q) xp[i][m][q] = xd[q];
       } else {  // 2-bit word t covers 8 x dwords: pairs (j, j+8)
 #pragma unroll
         for (int t = 0; t < WORDS; ++t)
