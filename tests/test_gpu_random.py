@@ -15,7 +15,7 @@ from parity import ODT, assert_close, dev, f32
 
 pytestmark = pytest.mark.gpu
 
-SEEDS = list(range(12))
+SEEDS = list(range(48))
 XDT = [torch.bfloat16, torch.float16]
 
 
