@@ -80,11 +80,12 @@ def test_linear_forward_validation(kw, code):
 
 
 def test_transcoded_widths_need_room_for_their_codes():
-    # 1- and 3-bit codes are rewritten as nibbles (N*K/2 bytes), 5- and 6-bit
-    # codes as bytes (N*K)
+    # 1-, 2- and 3-bit codes are rewritten as nibbles (N*K/2 bytes), 5- and
+    # 6-bit codes as bytes (N*K); 4- and 8-bit codes are used as they are
     L = qlq.lib()
     base = L.qlq_linear_workspace_size(2048, 4096, 11008, 4, 128, qlq.QLQ_BF16)
-    for bits, per in ((1, 0.5), (3, 0.5), (5, 1), (6, 1)):
+    assert L.qlq_linear_workspace_size(2048, 4096, 11008, 8, 128, qlq.QLQ_BF16) == base
+    for bits, per in ((1, 0.5), (2, 0.5), (3, 0.5), (5, 1), (6, 1)):
         assert L.qlq_linear_workspace_size(2048, 4096, 11008, bits, 128, qlq.QLQ_BF16) >= base + 11008 * 4096 * per
     assert L.qlq_linear_workspace_size(4, 4096, 11008, 3, 128, qlq.QLQ_BF16) == 0   # skinny: none
 
