@@ -234,11 +234,16 @@ gemv_pair_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
 //    groups when G >= 32*NCH, so a row needs one scale and one bias load per
 //    group the lane touches (group size is a template parameter);
 //  * the x loads are issued first, then every code / scale / bias load of the
-//    wave, then x goes to LDS: one memory round trip per wave;
+//    wave (codes through one buffer descriptor per row, all of them with the
+//    non-temporal policy: each byte is read once), then x goes to LDS: one
+//    memory round trip per wave;
+//  * after the barrier the lane reads all its x chunks out of LDS before
+//    anything waits for the weights, and the chunk loop has no branch;
 //  * 1-, 3-, 5- and 6-bit codes: code j and code j + 16 of the chunk's 32 are
 //    taken out of its BITS-word stream at compile-time offsets and joined
-//    into one 16-bit pair, against the x pair (x_j, x_j+16) (at 3, 5 and 6
-//    bits no two codes sit 16 bits apart in one word).
+//    into one 16-bit pair, against the x pair (x_j, x_j+16), which the block
+//    forms once while staging x (at 3, 5 and 6 bits no two codes sit 16 bits
+//    apart in one word).
 // ---------------------------------------------------------------------------
 template <int BITS> constexpr bool kStreamPairs = BITS == 1 || BITS == 3 || BITS == 5 || BITS == 6;
 

@@ -10,8 +10,9 @@
 // itself: it reads the whole rows for their absmax (the scale of quant_a),
 // then quantizes only its own 128 k into LDS, in the chunk order of the
 // unpacked weight (int4.hpp).  A lane takes 4 columns; each of the 4 waves
-// takes two groups of 8 k-pair rows, loads them as one dword per row,
-// transposes and unpacks them to 16 (code - 8), and accumulates int8 dot
+// takes two groups of 8 k-pair rows, loads them as one dword per row (with
+// the non-temporal policy: each weight byte is read once), transposes and
+// unpacks them to 16 (code - 8), and accumulates int8 dot
 // products of four into int32 per row of x.  The waves' sums meet in LDS and
 // the block writes one exact int32 partial per (row, column).  A second
 // kernel adds the partials of an output, takes the factor 16 off (>> 4) and
