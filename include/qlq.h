@@ -77,8 +77,12 @@ enum qlq_dtype { QLQ_F32 = 0, QLQ_F16 = 1, QLQ_BF16 = 2 };
  *  pergroup_linear docstring in "cider/ops.py".)
  *
  *   w       [N, K] fp32, finite.
- *   packed  [N, K*bits/32] uint32 (out).  Code k of a row sits at bit offset
- *           bits*(k mod (32/bits)) of word k / (32/bits) (LSB first).
+ *   packed  [N, K*bits/32] uint32 (out).  A row's codes form one bit stream,
+ *           least significant bit first: code k fills stream bits
+ *           bits*k .. bits*k + bits - 1, and stream bit i is bit i mod 32 of
+ *           word i / 32.  For bits in {1, 2, 4, 8} this puts code k at bit
+ *           offset bits*(k mod (32/bits)) of word k / (32/bits); 3-, 5- and
+ *           6-bit codes may straddle two words.
  *   scales, biases  [N, K/group_size] of sb_dtype (out).
  *
  * Per group of group_size consecutive K values: mn, mx = fp32 min and max;
@@ -87,7 +91,7 @@ enum qlq_dtype { QLQ_F32 = 0, QLQ_F16 = 1, QLQ_BF16 = 2 };
  * 0, 2^bits - 1) with the subtraction and the division in fp32 against the
  * stored scale and bias (rint rounds half to even).
  *
- * bits in {2, 4, 8}; group_size in {32, 64, 128}; K % group_size == 0.
+ * bits in {1, ..., 6, 8}; group_size in {32, 64, 128}; K % group_size == 0.
  * Synchronises `stream`.  Returns QLQ_ERR_DATA (outputs unspecified) if a
  * weight is not finite or a stored scale/bias overflows sb_dtype.
  */
@@ -98,6 +102,7 @@ QLQ_API int qlq_pack(const float* w, int64_t N, int64_t K, int bits, int group_s
 /*
  * qlq_unpack - packed [N, K*bits/32] uint32 -> codes [N, K] uint8 (one code
  * per byte).  Bit-exact inverse of the packing described under qlq_pack.
+ * bits in {1, ..., 6, 8}; K*bits % 32 == 0 (QLQ_ERR_INVALID_ARG otherwise).
  */
 QLQ_API int qlq_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits,
                        uint8_t* codes, void* stream);
@@ -106,6 +111,7 @@ QLQ_API int qlq_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits,
  * qlq_dequantize - w[n, k] = scale[n, g]*q[n, k] + bias[n, g] with
  * g = k / group_size, computed as one fp32 fused multiply-add (single
  * rounding), out [N, K] fp32.  ("Struct QuantizedLinear", dequantized_weight.)
+ * bits, group_size and the shape limits as for qlq_pack.
  */
 QLQ_API int qlq_dequantize(const uint32_t* packed, const void* scales, const void* biases,
                            int sb_dtype, int64_t N, int64_t K, int bits, int group_size,
