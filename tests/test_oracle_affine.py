@@ -194,7 +194,7 @@ def test_degenerate_group_takes_unit_scale():
         assert np.array_equal(affine.affine_dequantize(q, s, b, 64), w.astype(np.float64))
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 def test_idempotent_on_exact_groups(bits):
     """Groups built as s*q + b with s a power of two, b a multiple of s and
     both extreme codes present re-quantize to the same codes and parameters."""
