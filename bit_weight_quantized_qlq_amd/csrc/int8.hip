@@ -107,7 +107,11 @@ __device__ __forceinline__ void store(int8_t* tile, const uint32_t (&bw)[8], int
 // acc * sb[g, n] at every group boundary of a wave's k-steps (a group longer
 // than a wave's half of an iteration is flushed once per half: the scale is
 // the same, the sum is linear), and y = acc_f * sa[m] (+ bias).  The int32
-// partial of one flush is below 2^24, so its conversion is exact.
+// partial of one flush is below 2^24, so its conversion is exact.  With one
+// flush per k-iteration (groups of 128 or 256) the int32 sums alternate
+// between two register sets: iteration it's sums are rescaled between the
+// MFMAs of iteration it + 1, one 32x32 sub-tile per k-step, in the same
+// order as a flush at the end of the iteration would take them.
 //
 // BSRC != 0: b is packed int4 [K/2, N] (namespace w4), loaded into registers
 // one tile ahead and written to the B half of the ring slot after the MFMAs
@@ -125,6 +129,8 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const void* __restrict__ b, int M
                 "int4 B: 128 k-pair rows x 128 columns, 32 bytes per thread, double buffer");
   constexpr int FS = PG == 0 ? C::QN : (PG / KS < C::QN ? PG / KS : C::QN);  // k-steps per flush
   constexpr int NF = C::QN / FS;                                              // flushes per k-iteration
+  constexpr bool PIPE = PG != 0 && NF == 1;  // flushes overlap the next iteration's MFMAs
+  static_assert(!PIPE || 4 % C::QN == 0, "whole sub-tiles per k-step");
   // the ring during the K loop, then the 64 KiB of int32 partial sums that
   // join the two k-halves
   __shared__ __attribute__((aligned(16))) int8_t smem[STAGES * C::STAGE];
@@ -197,6 +203,66 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const void* __restrict__ b, int M
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t) QLQ_ISSUE(t);
   if constexpr (W4) w4::store<BK>(smem + C::TILE, bw, rg, cg);
+  if constexpr (PIPE) {
+    i32x16_v acc2[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc2[i][j] = i32x16_v{};
+    float sc0[2] = {0.0f, 0.0f}, sc1[2] = {0.0f, 0.0f};
+    // rescale sub-tile t of the int32 sums `sums` into accf and clear it
+    auto flush_tile = [&](i32x16_v (&sums)[2][2], const float (&scl)[2], int t) {
+      const int i = t >> 1, j = t & 1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) accf[i][j][e] = __builtin_fmaf((float)sums[i][j][e], scl[j], accf[i][j][e]);
+      sums[i][j] = i32x16_v{};
+    };
+    // k-iteration it: MFMAs into cur, the previous iteration's sums (prev,
+    // scales scp) rescaled between them; this iteration's scales into scc
+    auto step = [&](int it, i32x16_v (&cur)[2][2], i32x16_v (&prev)[2][2], float (&scc)[2], float (&scp)[2]) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(C::VMCNT) : "memory");
+      // scp was loaded an iteration ago and the wait above has drained it:
+      // from here on it is an ordinary value (no wait on the newer loads)
+      asm volatile("" : "+v"(scp[0]), "+v"(scp[1]));
+      {
+        const int g = min((it * BK + kh * C::QN * KS) / PG, ng - 1);  // past K: zero sums
+#pragma unroll
+        for (int j = 0; j < 2; ++j) scc[j] = sb[(int64_t)g * N + ncol[j]];
+      }
+      QLQ_ISSUE(it + STAGES - 1);
+      const int8_t* st_ = smem + (it % STAGES) * C::STAGE;
+      u32x4_v af[2][C::QN], bf[2][C::QN];
+#pragma unroll
+      for (int q = 0; q < C::QN; ++q)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          af[i][q] = *reinterpret_cast<const u32x4_v*>(st_ + aoff[i][q]);
+          bf[i][q] = *reinterpret_cast<const u32x4_v*>(st_ + boff[i][q]);
+        }
+#pragma unroll
+      for (int q = 0; q < C::QN; ++q) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) cur[i][j] = mma_i8(af[i][q], bf[j][q], cur[i][j]);
+#pragma unroll
+        for (int t = q * 4 / C::QN; t < (q + 1) * 4 / C::QN; ++t) flush_tile(prev, scp, t);
+      }
+    };
+    int it = 0;
+    for (; it + 1 < nk; it += 2) {
+      step(it, acc, acc2, sc0, sc1);
+      step(it + 1, acc2, acc, sc1, sc0);
+    }
+    if (it < nk) {
+      step(it, acc, acc2, sc0, sc1);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) flush_tile(acc, sc0, t);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) flush_tile(acc2, sc1, t);
+    }
+  } else
   for (int it = 0; it < nk; ++it) {
     // this thread's loads of tile it are done when at most the later
     // STAGES-2 tiles' loads are outstanding; then the barrier
