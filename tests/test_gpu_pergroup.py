@@ -44,7 +44,12 @@ def _case(M, K, N, G, xdt, seed, bias=True):
 
 @pytest.mark.parametrize("xdt", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("shape", [(2, 256, 45, 64), (37, 640, 130, 128), (130, 2304, 257, 256),
-                                   (1, 256, 45, 64), (1, 1088, 130, 64), (1, 2304, 257, 256)])
+                                   (1, 256, 45, 64), (1, 1088, 130, 64), (1, 2304, 257, 256),
+                                   # one, two and four 256-wide k-iterations with groups of
+                                   # 128 and 256 (the GEMM's per-group sums alternate between
+                                   # two register sets per k-iteration)
+                                   (5, 128, 33, 128), (67, 512, 129, 128), (3, 1024, 70, 256),
+                                   (9, 256, 64, 256)])
 def test_forward_ragged(xdt, shape):
     M, K, N, G = shape
     y, y_ref, D = _case(M, K, N, G, xdt, seed=M * 7 + K + N)
