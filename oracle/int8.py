@@ -92,11 +92,31 @@ def quantize_rows_int8_clip(w, clip_percentile):
     return q, s
 
 
+def exact_int_matmul(a, b):
+    """Exact integer product ``a [M, K] @ b [K, N]`` returned as int64.
+
+    When ``max|a| * max|b| * K < 2^53`` every partial sum, in whatever order a
+    library adds the terms, is an integer of magnitude below 2^53, which fp64
+    holds exactly; the product is then taken as an fp64 matrix product.  Any
+    larger bound takes the int64 product.
+    """
+    a = np.asarray(a)
+    b = np.asarray(b)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("shapes do not chain")
+    K = a.shape[1]
+    amax = int(np.abs(a.astype(np.int64)).max()) if a.size else 0
+    bmax = int(np.abs(b.astype(np.int64)).max()) if b.size else 0
+    if amax * bmax * max(K, 1) < 2 ** 53:
+        return (a.astype(np.float64) @ b.astype(np.float64)).astype(np.int64)
+    return a.astype(np.int64) @ b.astype(np.int64)
+
+
 def int8_matmul_int32(a, b):
-    """Exact ``a [M, K] @ b [N, K]^T`` in int64 (equals int32 when it fits)."""
-    a = np.asarray(a, dtype=np.int8).astype(np.int64)
-    b = np.asarray(b, dtype=np.int8).astype(np.int64)
-    return a @ b.T
+    """Exact ``a [M, K] @ b [N, K]^T`` as int64 (equals int32 when it fits)."""
+    a = np.asarray(a, dtype=np.int8)
+    b = np.asarray(b, dtype=np.int8)
+    return exact_int_matmul(a, b.T)
 
 
 def w8a8_forward(x, wq, sw, bias=None):
@@ -115,6 +135,6 @@ def w8a8_forward(x, wq, sw, bias=None):
     y = acc.astype(np.float64) * sx64 * sw64
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float64)[None, :]
-    absacc = np.abs(xq.astype(np.int64)) @ np.abs(np.asarray(wq, dtype=np.int64)).T
+    absacc = exact_int_matmul(np.abs(xq.astype(np.int64)), np.abs(np.asarray(wq, dtype=np.int64)).T)
     D = absacc.astype(np.float64) * sx64 * np.abs(sw64)
     return xq, sx, acc, y, D

@@ -28,7 +28,7 @@ quantizer):
 
 import numpy as np
 
-from .int8 import quantize_rows_int8
+from .int8 import exact_int_matmul, quantize_rows_int8
 
 
 def quantize_groups_int8(w, group_size):
@@ -80,11 +80,16 @@ def pergroup_forward(x, q, scale, group_size, bias=None):
     else:
         xq, sx = quantize_rows_int8(x)
         xg = xq.astype(np.int64).reshape(M, ng, G)
-        acc = np.einsum("mgk,ngk->mgn", xg, qg)               # exact int64 [M, ng, N]
-        absacc = np.einsum("mgk,ngk->mgn", np.abs(xg), np.abs(qg))
+        y = np.zeros((M, N), dtype=np.float64)
+        D = np.zeros((M, N), dtype=np.float64)
+        for g in range(ng):                                    # one exact int8 sum per group
+            acc = exact_int_matmul(xg[:, g, :], qg[:, g, :].T)  # [M, N]
+            absacc = exact_int_matmul(np.abs(xg[:, g, :]), np.abs(qg[:, g, :]).T)
+            y += acc.astype(np.float64) * s[g][None, :]
+            D += absacc.astype(np.float64) * np.abs(s[g])[None, :]
         sx64 = sx.astype(np.float64)[:, None]
-        y = (acc.astype(np.float64) * s[None, :, :]).sum(axis=1) * sx64
-        D = (absacc.astype(np.float64) * np.abs(s)[None, :, :]).sum(axis=1) * sx64
+        y = y * sx64
+        D = D * sx64
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float64)[None, :]
     return y, D

@@ -24,7 +24,7 @@ Readings:
 
 import numpy as np
 
-from .int8 import quantize_rows_int8
+from .int8 import exact_int_matmul, quantize_rows_int8
 
 ZERO_POINT = 8
 
@@ -75,11 +75,11 @@ def w4a8_forward(x, packed, scale_w, bias=None, zero_point=ZERO_POINT):
     xq, sx = quantize_rows_int8(x)
     wv = unpack_weight_int4(packed).astype(np.int64) - zero_point     # [K, N]
     xi = xq.astype(np.int64)
-    acc = xi @ wv
+    acc = exact_int_matmul(xi, wv)
     sx64 = sx.astype(np.float64)[:, None]
     sw64 = np.asarray(scale_w, dtype=np.float32).astype(np.float64)[None, :]
     y = acc.astype(np.float64) * sx64 * sw64
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float64)[None, :]
-    D = (np.abs(xi) @ np.abs(wv)).astype(np.float64) * sx64 * np.abs(sw64)
+    D = exact_int_matmul(np.abs(xi), np.abs(wv)).astype(np.float64) * sx64 * np.abs(sw64)
     return xq, sx, acc, y, D

@@ -100,3 +100,39 @@ def test_w8a8_brute_force_fractions():
 def test_rejects_non_finite():
     with pytest.raises(ValueError):
         oi8.quantize_rows_int8(np.array([[1.0, np.nan]], dtype=np.float32))
+
+
+def test_exact_int_matmul_both_routes_against_python_ints():
+    # the fp64 route (bound below 2^53) and the int64 route (bound above it)
+    # must both give the exact integer sums
+    rng = np.random.default_rng(34)
+    a = rng.integers(-128, 128, size=(4, 300)).astype(np.int64)
+    b = rng.integers(-128, 128, size=(300, 5)).astype(np.int64)
+    big_a = a * (1 << 20)
+    big_b = b * (1 << 20)        # 2^27 * 2^27 * 300 > 2^53: int64 route, still < 2^63
+    for x, y in ((a, b), (big_a, big_b)):
+        c = oi8.exact_int_matmul(x, y)
+        assert c.dtype == np.int64
+        for i in range(4):
+            for j in range(5):
+                assert int(c[i, j]) == sum(int(x[i, k]) * int(y[k, j]) for k in range(300))
+
+
+def test_exact_int_matmul_cancelling_sums():
+    # products near 2^40 that cancel pairwise, leaving a sum whose low bits
+    # an inexact product would lose
+    K = 64
+    a = np.full((1, K), (1 << 20) + 1, dtype=np.int64)
+    b = np.full((K, 1), (1 << 20) - 1, dtype=np.int64)
+    b[::2] = -((1 << 20) - 1)
+    b[0] = (1 << 20) + 3
+    want = sum(int(a[0, k]) * int(b[k, 0]) for k in range(K))
+    assert int(oi8.exact_int_matmul(a, b)[0, 0]) == want
+
+
+def test_workload_sized_int8_product_matches_int64():
+    # the fp64 route on a 64 x 4096 x 64 block of int8 extremes equals int64
+    rng = np.random.default_rng(35)
+    a = rng.choice(np.array([-128, 127, -127, 0], dtype=np.int8), size=(64, 4096))
+    b = rng.choice(np.array([-128, 127, 1, -1], dtype=np.int8), size=(64, 4096))
+    assert np.array_equal(oi8.int8_matmul_int32(a, b), a.astype(np.int64) @ b.astype(np.int64).T)
