@@ -48,6 +48,9 @@ def test_clipped_weights_run_through_w8a8():
     from parity import assert_close
     inp = workloads.w8a8_inputs(64, 1024, 256, seed=9)
     wq, sw = qlq.qlq_quantize_rows_int8_clip(inp["w"].to(dev()), 99.9)
+    wq_ref, sw_ref = oracle.quantize_rows_int8_clip(inp["w"].numpy(), 99.9)
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    assert np.array_equal(sw.cpu().numpy().view(np.uint32), sw_ref.view(np.uint32))
     y = qlq.w8a8_linear_forward(inp["x"].to(dev()), wq, sw)
-    _, _, _, y_ref, D = oracle.w8a8_forward(f32(inp["x"]), wq.cpu().numpy(), sw.cpu().numpy())
+    _, _, _, y_ref, D = oracle.w8a8_forward(f32(inp["x"]), wq_ref, sw_ref)
     assert_close(y, y_ref, D, 1024, torch.float16, label="w8a8 on clipped weights")

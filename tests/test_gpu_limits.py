@@ -27,12 +27,15 @@ def test_w8a8_extreme_sum_at_max_k():
     w = torch.ones(N, K)
     w[5] = -1.0
     wq, sw = qlq.qlq_quantize_rows_int8(w.to(dev()))
+    wq_ref, sw_ref = oracle.quantize_rows_int8(w.numpy())
+    xq_ref, _ = oracle.quantize_rows_int8(f32(x))
+    assert np.array_equal(wq.cpu().numpy(), wq_ref) and np.array_equal(sw.cpu().numpy(), sw_ref)
     acc = qlq.qlq_int8_matmul_int32(qlq.qlq_quantize_rows_int8(x.to(dev()))[0], wq)
-    ref = oracle.int8_matmul_int32(oracle.quantize_rows_int8(f32(x))[0], wq.cpu().numpy())
+    ref = oracle.int8_matmul_int32(xq_ref, wq_ref)
     assert np.abs(ref).max() == 127 * 127 * K < 2 ** 31
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref)
     y = qlq.w8a8_linear_forward(x.to(dev()), wq, sw)
-    *_, y_ref, D = oracle.w8a8_forward(f32(x), wq.cpu().numpy(), sw.cpu().numpy())
+    *_, y_ref, D = oracle.w8a8_forward(f32(x), wq_ref, sw_ref)
     assert_close(y, y_ref, D, K, torch.bfloat16, label="w8a8 K max")  # half an output ulp exceeds the strict bound here
 
 
@@ -67,8 +70,11 @@ def test_pergroup_mv_at_k_cap():
     K, N, G = 16384, 96, 256
     inp = workloads.w8a8_inputs(1, K, N, x_dtype="bf16", bias=True, seed=77)
     q, sg = qlq.qlq_quantize_groups_int8(inp["w"].to(dev()), G)
+    q_ref, s_ref = oracle.quantize_groups_int8(inp["w"].numpy(), G)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(sg.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
     y = qlq.pergroup_linear_forward(inp["x"].to(dev()), q, sg, G, bias=inp["bias"].to(dev()))
-    y_ref, D = oracle.pergroup_forward(f32(inp["x"]), q.cpu().numpy(), sg.cpu().numpy(), G, bias=f32(inp["bias"]))
+    y_ref, D = oracle.pergroup_forward(f32(inp["x"]), q_ref, s_ref, G, bias=f32(inp["bias"]))
     assert_close(y, y_ref, D, K, torch.bfloat16, strict=True, label="pergroup M=1 K cap")
     with pytest.raises(qlq.QLQError) as e:
         qlq.pergroup_linear_forward(torch.zeros(1, K + G, dtype=torch.bfloat16, device=dev()),

@@ -75,11 +75,12 @@ def test_pack_rejects_out_of_set():
 def test_code_three_decodes_literally():
     """A byte the packer never emits (all fields = 3) decodes to +2."""
     M, K, N = 2, 64, 8
-    packed = torch.full((N // 4, K), 0xFF, dtype=torch.uint8, device=dev())
+    packed_host = np.full((N // 4, K), 0xFF, dtype=np.uint8)
+    packed = torch.from_numpy(packed_host).to(dev())
     x = torch.ones(M, K, dtype=torch.bfloat16, device=dev())
     ws = torch.ones(1, dtype=torch.bfloat16, device=dev())
     y = qlq.bitlinear_forward(x, packed, N, ws)
-    y_ref, _ = oracle.ternary_forward(np.ones((M, K)), packed.cpu().numpy(), N, 1.0)
+    y_ref, _ = oracle.ternary_forward(np.ones((M, K)), packed_host, N, 1.0)
     assert np.array_equal(f32(y), y_ref.astype(np.float32))
     assert (y_ref == 2 * K).all()
 
