@@ -81,8 +81,8 @@ int current_device_status() {
   } while (0)
 
 bool affine_bits_ok(int bits) { return (bits >= 1 && bits <= 6) || bits == 8; }
-// the packed width the GEMM runs on: 1- and 3-bit codes are transcoded to
-// the 4-bit layout, 5- and 6-bit codes to the 8-bit one
+// the packed width the GEMM runs on: 1-, 2- and 3-bit codes are transcoded
+// to the 4-bit layout, 5- and 6-bit codes to the 8-bit one
 int gemm_bits(int bits) { return bits <= 3 ? 4 : bits == 5 || bits == 6 ? 8 : bits; }
 bool transcoded_gemm(int bits) { return gemm_bits(bits) != bits; }
 
@@ -97,11 +97,14 @@ int check_affine_shape(int64_t N, int64_t K, int bits, int G) {
 }
 
 // The GEMM path takes 16-bit x with K a multiple of its 64-wide k-iteration.
-// The prefill GEMM addresses its operands through 32-bit buffer offsets: a
-// 128-row tile of x16 (256 K bytes) and the (s', b') table (4 (K/G) N bytes)
-// must stay below 2^31 bytes; other shapes take the skinny kernel.
+// The prefill GEMM addresses its operands through 32-bit buffer offsets: the
+// tallest x16 tile the launcher can pick (256 rows of 2 K bytes, chosen at
+// launch from the tile count), a 128-row tile of 8-bit codes (128 K bytes)
+// and the (s', b') table (4 (K/G) N bytes) must stay below 2^31 bytes; other
+// shapes take the skinny kernel.
+constexpr int64_t kGemmTallestTileRows = 256;
 bool takes_gemm(int64_t M, int64_t K, int64_t N, int G, int x_dtype) {
-  return x_dtype != QLQ_F32 && M > g_skinny_max_m && K % 64 == 0 && K * 256 < kMaxDim &&
+  return x_dtype != QLQ_F32 && M > g_skinny_max_m && K % 64 == 0 && K * 2 * kGemmTallestTileRows < kMaxDim &&
          (K / G) * ((N + 3) & ~(int64_t)3) * 4 < kMaxDim;
 }
 
@@ -221,9 +224,9 @@ QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
   if (int st = current_device_status()) return st;
   hipStream_t s = (hipStream_t)stream;
   if (gemm && transcoded_gemm(bits)) {
-    // 1, 3, 5, 6 bits: the codes are rewritten in the 4-bit (1, 3) or 8-bit
-    // (5, 6: one byte per code) packed layout, and that width's GEMM runs on
-    // them with the same scales and biases
+    // 1, 2, 3, 5, 6 bits: the codes are rewritten in the 4-bit (1, 2, 3) or
+    // 8-bit (5, 6: one byte per code) packed layout, and that width's GEMM
+    // runs on them with the same scales and biases
     uint32_t* codes = (uint32_t*)((char*)workspace +
                                   ((qlq::affine_gemm_workspace(M, K, N, group_size) + 255) & ~(size_t)255));
     const int wb = gemm_bits(bits);

@@ -8,8 +8,10 @@
 //
 // Arithmetic.  With per-row powers of two 2^e_m (x) and per-column 2^f_n (w):
 //   y[m,n] = 2^(e_m + f_n) * sum_k x16[m,k] * w16[n,k]  (+ bias[n])
-//   x16 = fp16(x * 2^-e_m)                  (exact: a bf16 or fp16 value
-//                                            rescaled into fp16 range)
+//   x16 = fp16(x * 2^-e_m)                  (exact for every element within
+//                                            2^24 of the row maximum; smaller
+//                                            ones fall into fp16 subnormals
+//                                            and round, far below the bound)
 //   w16 = fp16((s*q + b) * 2^-f_n)           (one rounding, 2^-11 relative)
 // Products of two fp16 values are exact in fp32; the MFMA accumulates in
 // fp32.  The dequantization costs one packed fp16 FMA per two codes:

@@ -280,3 +280,17 @@ def test_empty_batch_accepts_null_row_tensors():
     # a non-empty batch still needs them
     assert L.w8a8_linear_forward(None, qlq.QLQ_F16, 4, 64, B, A, 32, None, A, B, 1 << 20, None) == \
         qlq.QLQ_ERR_INVALID_ARG
+
+
+def test_gemm_bound_follows_the_tallest_tile():
+    # 2048 x 16256 outputs give 8 x 127 = 1016 tiles of 256 x 128, enough for
+    # the launcher to pick 256-row tiles; with K = 2^22 + 128 a 256-row tile
+    # of fp16 x spans 512 K > 2^31 bytes, beyond the GEMM's 32-bit buffer
+    # offsets, so the call takes the skinny kernel (no workspace)
+    L = qlq.lib()
+    M, N, G = 2048, 16256, 128
+    K_big = (1 << 22) + 128
+    assert 4 * (K_big // G) * N < 2 ** 31          # the (s', b') table alone would fit
+    assert L.qlq_linear_workspace_size(M, K_big, N, 4, G, qlq.QLQ_BF16) == 0
+    K_ok = (1 << 22) - 128
+    assert L.qlq_linear_workspace_size(M, K_ok, N, 4, G, qlq.QLQ_BF16) > 0
