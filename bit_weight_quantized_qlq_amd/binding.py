@@ -124,6 +124,37 @@ def _flatten(x):
     return x.reshape(-1, x.shape[-1]) if x.dim() != 2 else x
 
 
+def _shape(t, name, shape):
+    """Raise ValueError unless tensor ``t`` has exactly ``shape``."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _out_shape(out, M, N):
+    """An output tensor must hold exactly M*N elements with N innermost."""
+    if out is not None and (out.numel() != M * N or (out.dim() and out.shape[-1] != N)):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {M * N} elements as [..., {N}]")
+
+
+def _whole_groups(K, group_size):
+    return group_size > 0 and K % group_size == 0
+
+
+def _check_affine_operands(K, packed, scales, biases, bits, group_size):
+    """packed [N, K*bits/32]; scales and biases [N, K/group_size].  Shapes the
+    library rejects anyway (K not a whole number of words or groups) are left
+    to its own error codes."""
+    if packed.dim() != 2:
+        raise ValueError("packed must be 2-D")
+    N = packed.shape[0]
+    if bits > 0 and (K * bits) % 32 == 0:
+        _shape(packed, "packed", (N, K * bits // 32))
+    if _whole_groups(K, group_size):
+        _shape(scales, "scales", (N, K // group_size))
+        _shape(biases, "biases", (N, K // group_size))
+    return N
+
+
 # ------------------------------------------------------------------ affine
 def qlq_pack(w, bits=4, group_size=64, sb_dtype=torch.bfloat16):
     """Quantize fp32 weights [N, K]; returns (packed uint32 as int32, scales, biases)."""
@@ -138,6 +169,8 @@ def qlq_pack(w, bits=4, group_size=64, sb_dtype=torch.bfloat16):
 
 
 def qlq_unpack(packed, K, bits=4):
+    if packed.dim() == 2 and bits > 0 and (K * bits) % 32 == 0:
+        _shape(packed, "packed", (packed.shape[0], K * bits // 32))
     _dev(packed, "packed", torch.int32, 2)
     N = packed.shape[0]
     codes = torch.empty((N, K), dtype=torch.uint8, device=packed.device)
@@ -146,6 +179,7 @@ def qlq_unpack(packed, K, bits=4):
 
 
 def qlq_dequantize(packed, scales, biases, K, bits=4, group_size=64):
+    _check_affine_operands(K, packed, scales, biases, bits, group_size)
     _dev(packed, "packed", torch.int32, 2)
     _dev(scales, "scales", tuple(DTYPE_CODE))
     _dev(biases, "biases", scales.dtype)
@@ -163,6 +197,11 @@ def qlq_linear_workspace_size(M, K, N, bits, group_size, x_dtype):
 def qlq_linear_forward(x, packed, scales, biases, bits=4, group_size=64, bias=None, out=None,
                        workspace=None):
     """y = x . dequant(W)^T (+ bias) over the last axis of x."""
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    N = _check_affine_operands(K, packed, scales, biases, bits, group_size)
+    _shape(bias, "bias", (N,))
+    _out_shape(out, M, N)
     _dev(x, "x", tuple(DTYPE_CODE))
     _dev(packed, "packed", torch.int32, 2)
     _dev(scales, "scales")
@@ -170,8 +209,6 @@ def qlq_linear_forward(x, packed, scales, biases, bits=4, group_size=64, bias=No
     if bias is not None:
         _dev(bias, "bias", x.dtype, 1)
     x2 = _flatten(x)
-    M, K = x2.shape
-    N = packed.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     else:
@@ -206,13 +243,20 @@ def bitlinear_pack(t):
 
 def bitlinear_forward(x, packed, N, weight_scale, invert_weight_scale=False, bias=None, out=None):
     """y = sigma * x . decode(packed)^T (+ bias); weight_scale must have x's dtype."""
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    if N % 4 == 0:
+        _shape(packed, "packed", (N // 4, K))
+    if weight_scale.numel() != 1:
+        raise ValueError(f"weight_scale must hold one element, not {weight_scale.numel()}")
+    _shape(bias, "bias", (N,))
+    _out_shape(out, M, N)
     _dev(x, "x", tuple(DTYPE_CODE))
     _dev(packed, "packed", torch.uint8, 2)
     _dev(weight_scale, "weight_scale", x.dtype)
     if bias is not None:
         _dev(bias, "bias", x.dtype, 1)
     x2 = _flatten(x)
-    M, K = x2.shape
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     else:
@@ -260,14 +304,21 @@ def w8a8_workspace_size(M, K):
 
 
 def w8a8_linear_forward(x, w, scale_w, bias=None, out=None, workspace=None):
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D")
+    N = w.shape[0]
+    _shape(w, "w", (N, K))
+    _shape(scale_w, "scale_w", (N,))
+    _shape(bias, "bias", (N,))
+    _out_shape(out, M, N)
     _dev(x, "x", (torch.float16, torch.bfloat16))
     _dev(w, "w", torch.int8, 2)
     _dev(scale_w, "scale_w", torch.float32, 1)
     if bias is not None:
         _dev(bias, "bias", x.dtype, 1)
     x2 = _flatten(x)
-    M, K = x2.shape
-    N = w.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     else:
@@ -299,14 +350,22 @@ def pergroup_workspace_size(M, K):
 
 def pergroup_linear_forward(x, w, scale_w, group_size, bias=None, out=None, workspace=None):
     """Per-group int8 linear; M == 1 keeps x in floating point, M > 1 quantizes it."""
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D")
+    N = w.shape[0]
+    _shape(w, "w", (N, K))
+    if _whole_groups(K, group_size):
+        _shape(scale_w, "scale_w", (K // group_size, N))
+    _shape(bias, "bias", (N,))
+    _out_shape(out, M, N)
     _dev(x, "x", (torch.float16, torch.bfloat16))
     _dev(w, "w", torch.int8, 2)
     _dev(scale_w, "scale_w", torch.float32, 2)
     if bias is not None:
         _dev(bias, "bias", x.dtype, 1)
     x2 = _flatten(x)
-    M, K = x2.shape
-    N = w.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     else:
@@ -338,16 +397,22 @@ def w4a8_workspace_size(M, K, N):
 
 def w4a8_linear_forward(x, packed_w, scale_w, bias=None, out=None, workspace=None):
     """W4A8 linear: x [..., K] f16/bf16, packed_w uint8 [K/2, N], scale_w f32 [N]."""
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    if packed_w.dim() != 2:
+        raise ValueError("packed_w must be 2-D")
+    N = packed_w.shape[1]
+    if packed_w.shape[0] * 2 != K:
+        raise ValueError("packed_w must be [K/2, N]")
+    _shape(scale_w, "scale_w", (N,))
+    _shape(bias, "bias", (N,))
+    _out_shape(out, M, N)
     _dev(x, "x", (torch.float16, torch.bfloat16))
     _dev(packed_w, "packed_w", torch.uint8, 2)
     _dev(scale_w, "scale_w", torch.float32, 1)
     if bias is not None:
         _dev(bias, "bias", x.dtype, 1)
     x2 = _flatten(x)
-    M, K = x2.shape
-    N = packed_w.shape[1]
-    if packed_w.shape[0] * 2 != K:
-        raise ValueError("packed_w must be [K/2, N]")
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     else:
