@@ -54,6 +54,7 @@ SIGNATURES = {
     "qlq_int8_matmul_int32": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "w8a8_workspace_size": (_sz, [_i64, _i64]),
     "w8a8_linear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "w8a8_linear_forward_noalloc": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
     "qlq_quantize_groups_int8": (_int, [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp]),
     "pergroup_workspace_size": (_sz, [_i64, _i64]),
     "pergroup_linear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _int, _vp, _vp, _vp, _sz, _vp]),
@@ -329,6 +330,40 @@ def w8a8_linear_forward(x, w, scale_w, bias=None, out=None, workspace=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().w8a8_linear_forward(_ptr(x2), DTYPE_CODE[x.dtype], M, K, _ptr(w), _ptr(scale_w), N,
                                      _ptr(bias), _ptr(out), _ptr(workspace), ws_bytes, _stream(x)))
+    return out.reshape(*x.shape[:-1], N)
+
+
+# Scratch bytes the allocation-free W8A8 call holds on each GPU
+# (QLQ_W8A8_NOALLOC_SCRATCH_BYTES in include/qlq.h).
+W8A8_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def w8a8_linear_forward_noalloc(x, w, scale_w, bias=None, out=None):
+    """w8a8_linear_forward without a workspace: the library's static device
+    scratch holds the quantized activations.  The binding allocates ``out``
+    when none is given; pass ``out`` to keep the call free of allocations.
+    Calls that overlap on one GPU race on the shared scratch."""
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D")
+    N = w.shape[0]
+    _shape(w, "w", (N, K))
+    _shape(scale_w, "scale_w", (N,))
+    _shape(bias, "bias", (N,))
+    _out_shape(out, M, N)
+    _dev(x, "x", (torch.float16, torch.bfloat16))
+    _dev(w, "w", torch.int8, 2)
+    _dev(scale_w, "scale_w", torch.float32, 1)
+    if bias is not None:
+        _dev(bias, "bias", x.dtype, 1)
+    x2 = _flatten(x)
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _dev(out, "out", x.dtype)
+    _check(lib().w8a8_linear_forward_noalloc(_ptr(x2), DTYPE_CODE[x.dtype], M, K, _ptr(w), _ptr(scale_w), N,
+                                             _ptr(bias), _ptr(out), _stream(x)))
     return out.reshape(*x.shape[:-1], N)
 
 

@@ -342,9 +342,14 @@ QLQ_API size_t w8a8_workspace_size(int64_t M, int64_t K) {
   return q + (size_t)M * sizeof(float);
 }
 
-QLQ_API int w8a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* w,
-                                const float* scale_w, int64_t N, const void* bias, void* y, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of w8a8_linear_forward and its allocation-free variant, apart
+// from where the quantized activations go.
+int check_w8a8_args(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* w, const float* scale_w,
+                    int64_t N, const void* bias, const void* y) {
   QLQ_REQUIRE(((x && y) || M == 0) && w && scale_w, QLQ_ERR_INVALID_ARG, "null pointer");
   QLQ_REQUIRE(M >= 0 && M < kMaxDim && N >= 1 && N < kMaxDim && K >= 16, QLQ_ERR_INVALID_ARG, "invalid shape");
   QLQ_REQUIRE(K % 16 == 0, QLQ_ERR_INVALID_ARG, "K=%lld is not a multiple of 16", (long long)K);
@@ -354,18 +359,89 @@ QLQ_API int w8a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K
                   (!bias || aligned(bias, 2)),
               QLQ_ERR_ALIGNMENT, "misaligned pointer");
   QLQ_REQUIRE((M + 127) / 128 <= 65535, QLQ_ERR_UNSUPPORTED, "M too large for one launch");
+  return QLQ_OK;
+}
+
+// quant_a(x) into xq [M, K] and sx [M] at the aligned offset of
+// w8a8_workspace_size, then the int8 GEMM with the scale epilogue.
+int run_w8a8(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* w, const float* scale_w, int64_t N,
+             const void* bias, void* y, void* buf, hipStream_t s) {
+  int8_t* xq = (int8_t*)buf;
+  float* sx = (float*)((char*)buf + (((size_t)M * (size_t)K + 255) & ~(size_t)255));
+  if (int st = hip_status(qlq::launch_quantize_rows_int8(x, x_dtype, M, K, xq, sx, s), "activation quant"))
+    return st;
+  return hip_status(qlq::launch_int8_gemm(xq, w, M, N, K, sx, scale_w, bias, x_dtype, y, s), "int8 gemm");
+}
+
+}  // namespace
+
+// Scratch of w8a8_linear_forward_noalloc: quant_a(x) and its row scales live
+// in this file-scope device array instead of a caller workspace.  Every GPU
+// the library runs on holds its own copy, at its own address, until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: host code uses only the per-device address taken below.
+constexpr size_t kNoAllocScratchBytes = QLQ_W8A8_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // device address of `scratch`, per device; taken once
+
+// The current device's copy of `scratch`: its address is looked up the first
+// time a call runs on that device, with that device current.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return fail(QLQ_ERR_DEVICE, "no current HIP device");
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(QLQ_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+QLQ_API int w8a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* w,
+                                const float* scale_w, int64_t N, const void* bias, void* y, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (int st = check_w8a8_args(x, x_dtype, M, K, w, scale_w, N, bias, y)) return st;
   if (M == 0) return ok();
   const size_t need = w8a8_workspace_size(M, K);
   QLQ_REQUIRE(workspace && workspace_bytes >= need, QLQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
               need, workspace ? workspace_bytes : (size_t)0);
   QLQ_REQUIRE(aligned(workspace, 16), QLQ_ERR_ALIGNMENT, "workspace not 16-byte aligned");
   if (int st = current_device_status()) return st;
-  hipStream_t s = (hipStream_t)stream;
-  int8_t* xq = (int8_t*)workspace;
-  float* sx = (float*)((char*)workspace + (((size_t)M * (size_t)K + 255) & ~(size_t)255));
-  if (int st = hip_status(qlq::launch_quantize_rows_int8(x, x_dtype, M, K, xq, sx, s), "activation quant"))
-    return st;
-  return hip_status(qlq::launch_int8_gemm(xq, w, M, N, K, sx, scale_w, bias, x_dtype, y, s), "int8 gemm");
+  return run_w8a8(x, x_dtype, M, K, w, scale_w, N, bias, y, workspace, (hipStream_t)stream);
+}
+
+QLQ_API int w8a8_linear_forward_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* w,
+                                        const float* scale_w, int64_t N, const void* bias, void* y, void* stream) {
+  if (int st = check_w8a8_args(x, x_dtype, M, K, w, scale_w, N, bias, y)) return st;
+  if (M == 0) return ok();
+  const size_t need = w8a8_workspace_size(M, K);
+  QLQ_REQUIRE(need <= kNoAllocScratchBytes, QLQ_ERR_WORKSPACE,
+              "M=%lld, K=%lld need %zu bytes of scratch; the allocation-free call holds at most %zu "
+              "(use w8a8_linear_forward with a workspace)",
+              (long long)M, (long long)K, need, kNoAllocScratchBytes);
+  if (int st = current_device_status()) return st;
+  void* buf = nullptr;
+  if (int st = scratch_on_current_device(&buf)) return st;
+  // every byte of the scratch that the GEMM reads (xq and sx) is written by
+  // the quantizer first in the same stream, so nothing needs clearing
+  return run_w8a8(x, x_dtype, M, K, w, scale_w, N, bias, y, buf, (hipStream_t)stream);
 }
 
 QLQ_API int qlq_quantize_groups_int8(const void* w, int w_dtype, int64_t N, int64_t K, int group_size,

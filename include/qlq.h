@@ -256,6 +256,32 @@ QLQ_API int w8a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K
                                 const void* bias, void* y, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * w8a8_linear_forward_noalloc - w8a8_linear_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, kernels and
+ * result, with no workspace argument.  quant_a(x) and sx go to a static
+ * device array of QLQ_W8A8_NOALLOC_SCRATCH_BYTES bytes that each GPU the
+ * library runs on holds until the process ends; its address is looked up
+ * once per device, on the first call there.  The call allocates nothing.
+ *
+ *   Arguments as w8a8_linear_forward without workspace / workspace_bytes.
+ *   w8a8_workspace_size(M, K) must not exceed QLQ_W8A8_NOALLOC_SCRATCH_BYTES
+ *   (else QLQ_ERR_WORKSPACE, checked before any HIP call): M*K up to about
+ *   16 million int8 values, e.g. up to 4092 rows at K = 4096.
+ *
+ * All calls on one GPU share that GPU's array, which keeps the last call's
+ * contents: two calls that overlap on one GPU (different streams without an
+ * ordering between them, or different host threads) race on it and give
+ * undefined results.  Calls ordered on one stream are safe; nothing in the
+ * array needs to start at zero (the quantizer writes every byte the GEMM
+ * reads).
+ */
+#define QLQ_W8A8_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+QLQ_API int w8a8_linear_forward_noalloc(const void* x, int x_dtype, int64_t M, int64_t K,
+                                        const int8_t* w, const float* scale_w, int64_t N,
+                                        const void* bias, void* y, void* stream);
+
 /* ------------------------------------------------------------------------
  * Per-group int8 weights ("cider/ops.py": pergroup_linear)
  * ------------------------------------------------------------------------ */

@@ -294,3 +294,27 @@ def test_gemm_bound_follows_the_tallest_tile():
     assert L.qlq_linear_workspace_size(M, K_big, N, 4, G, qlq.QLQ_BF16) == 0
     K_ok = (1 << 22) - 128
     assert L.qlq_linear_workspace_size(M, K_ok, N, 4, G, qlq.QLQ_BF16) > 0
+
+
+def test_noalloc_w8a8_validation():
+    L = qlq.lib()
+    text = open(HEADER).read()
+    assert "#define QLQ_W8A8_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
+    assert qlq.W8A8_NOALLOC_SCRATCH_BYTES == 16 << 20
+    f = L.w8a8_linear_forward_noalloc
+    ok = dict(x=A, x_dtype=qlq.QLQ_F16, M=16, K=64, w=B, sw=A, N=32, bias=None, y=A)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["x"], a["x_dtype"], a["M"], a["K"], a["w"], a["sw"], a["N"], a["bias"], a["y"], None)
+
+    assert call(x=None) == qlq.QLQ_ERR_INVALID_ARG
+    assert call(K=40) == qlq.QLQ_ERR_INVALID_ARG
+    assert call(x_dtype=qlq.QLQ_F32) == qlq.QLQ_ERR_UNSUPPORTED
+    assert call(x=ODD) == qlq.QLQ_ERR_ALIGNMENT
+    assert call(M=0) == 0 and call(M=0, x=None, y=None) == 0
+    # beyond the static scratch: rejected before any HIP call, on any machine
+    assert L.w8a8_workspace_size(4093, 4096) > qlq.W8A8_NOALLOC_SCRATCH_BYTES
+    assert call(M=4093, K=4096) == qlq.QLQ_ERR_WORKSPACE
+    assert "scratch" in qlq.last_error()
