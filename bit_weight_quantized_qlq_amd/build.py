@@ -3,8 +3,10 @@
     python -m bit_weight_quantized_qlq_amd.build [--verbose]
 
 Sources under csrc/ are compiled in parallel into csrc/../_build/*.o and
-linked into bit_weight_quantized_qlq_amd/libqlq.so.  The build always
-recompiles (it is the "does it build" check); nothing is cached across calls.
+linked into bit_weight_quantized_qlq_amd/libqlq.so; the read-rate probes the
+benchmark uses (csrc/probe.hip) go into their own libqlq_probe.so.  The build
+always recompiles (it is the "does it build" check); nothing is cached across
+calls.
 """
 
 import argparse
@@ -20,6 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqlq.so")
 SOURCES = ["api.cpp", "pack.hip", "gemv.hip", "gemm.hip", "ternary.hip", "int8.hip", "pergroup.hip", "w4a8.hip"]
+PROBE_LIB = os.path.join(PKG, "libqlq_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -50,21 +54,28 @@ def _compile(src, extra, verbose):
     return obj
 
 
-def build(verbose=False, extra_flags=None, jobs=None):
-    """Compile every source and link libqlq.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    extra = list(extra_flags or [])
-    jobs = jobs or min(len(SOURCES), 8)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False, extra_flags=None, jobs=None):
+    """Compile every source, link libqlq.so and libqlq_probe.so; returns the
+    path of libqlq.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = list(extra_flags or [])
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = jobs or min(len(srcs), 8)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, extra, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 
