@@ -65,15 +65,25 @@ def _link(objs, lib, verbose):
     os.replace(tmp, lib)
 
 
-def build(verbose=False, extra_flags=None, jobs=None):
-    """Compile every source, link libqlq.so and libqlq_probe.so; returns the
-    path of libqlq.so."""
+def build(verbose=False, extra_flags=None, jobs=None, only=None):
+    """Compile every source (or only those named in `only`, relinking with the
+    objects already built for the others), link libqlq.so and
+    libqlq_probe.so; returns the path of libqlq.so."""
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra_flags or [])
     srcs = SOURCES + PROBE_SOURCES
-    jobs = jobs or min(len(srcs), 8)
+    todo = srcs if not only else [s for s in srcs if s in only]
+    if only and len(todo) != len(set(only)):
+        raise ValueError(f"unknown sources {sorted(set(only) - set(srcs))}; sources: {srcs}")
+    jobs = jobs or min(len(todo), 8)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, extra, verbose), srcs)))
+        objs = dict(zip(todo, ex.map(lambda s: _compile(s, extra, verbose), todo)))
+    for s in srcs:
+        if s not in objs:
+            o = os.path.join(BUILD, os.path.splitext(s)[0] + ".o")
+            if not os.path.exists(o):
+                raise RuntimeError(f"{o} is not built: run a full build first")
+            objs[s] = o
     _link([objs[s] for s in SOURCES], LIB, verbose)
     _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
@@ -83,8 +93,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("-D", action="append", default=[], help="extra preprocessor define")
+    ap.add_argument("--only", nargs="+", help="compile only these sources (e.g. gemv.hip) and relink")
     args = ap.parse_args()
-    path = build(verbose=args.verbose, extra_flags=[f"-D{d}" for d in args.D])
+    path = build(verbose=args.verbose, extra_flags=[f"-D{d}" for d in args.D], only=args.only)
     print(path)
 
 
