@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     bitlinear_pack, bitlinear_forward,
     qlq_quantize_rows_int8, qlq_quantize_rows_int8_clip, qlq_int8_matmul_int32, w8a8_workspace_size, w8a8_linear_forward,
     w8a8_linear_forward_noalloc, W8A8_NOALLOC_SCRATCH_BYTES,
+    qlq_set_w8a8_fused_quant, qlq_get_w8a8_fused_quant,
     qlq_quantize_groups_int8, pergroup_workspace_size, pergroup_linear_forward,
     w4a8_pack_weight_int4, w4a8_workspace_size, w4a8_linear_forward,
     qlq_device_check, qlq_version,

@@ -47,6 +47,8 @@ SIGNATURES = {
                                   _vp, _vp, _sz, _vp]),
     "qlq_set_skinny_max_m": (_int, [_int]),
     "qlq_get_skinny_max_m": (_int, []),
+    "qlq_set_w8a8_fused_quant": (_int, [_int]),
+    "qlq_get_w8a8_fused_quant": (_int, []),
     "bitlinear_pack": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "bitlinear_forward": (_int, [_vp, _int, _i64, _i64, _vp, _i64, _vp, _int, _vp, _vp, _vp]),
     "qlq_quantize_rows_int8": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp]),
@@ -298,6 +300,16 @@ def qlq_int8_matmul_int32(a, b):
     c = torch.empty((M, N), dtype=torch.int32, device=a.device)
     _check(lib().qlq_int8_matmul_int32(_ptr(a), _ptr(b), M, N, K, _ptr(c), _stream(a)))
     return c
+
+
+def qlq_set_w8a8_fused_quant(on):
+    """Select where the W8A8 activation quantizer runs: 0 before the GEMM
+    (default), 1 inside it (bit-identical results)."""
+    _check(lib().qlq_set_w8a8_fused_quant(int(on)))
+
+
+def qlq_get_w8a8_fused_quant():
+    return int(lib().qlq_get_w8a8_fused_quant())
 
 
 def w8a8_workspace_size(M, K):

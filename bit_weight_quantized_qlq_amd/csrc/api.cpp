@@ -16,6 +16,7 @@ namespace {
 
 thread_local std::string g_err;
 int g_skinny_max_m = 8;
+int g_w8a8_fused_quant = 0;  // W8A8: activation quantizer inside the GEMM (1) or before it (0)
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -134,6 +135,13 @@ QLQ_API int qlq_set_skinny_max_m(int m) {
   return ok();
 }
 QLQ_API int qlq_get_skinny_max_m(void) { return g_skinny_max_m; }
+
+QLQ_API int qlq_set_w8a8_fused_quant(int on) {
+  QLQ_REQUIRE(on == 0 || on == 1, QLQ_ERR_INVALID_ARG, "fused activation quant must be 0 or 1 (got %d)", on);
+  g_w8a8_fused_quant = on;
+  return ok();
+}
+QLQ_API int qlq_get_w8a8_fused_quant(void) { return g_w8a8_fused_quant; }
 
 // ----------------------------------------------------------------- affine
 QLQ_API int qlq_pack(const float* w, int64_t N, int64_t K, int bits, int group_size, uint32_t* packed,
@@ -363,11 +371,19 @@ int check_w8a8_args(const void* x, int x_dtype, int64_t M, int64_t K, const int8
 }
 
 // quant_a(x) into xq [M, K] and sx [M] at the aligned offset of
-// w8a8_workspace_size, then the int8 GEMM with the scale epilogue.
+// w8a8_workspace_size, then the int8 GEMM with the scale epilogue; or, with
+// the fused quantizer selected, only sx (a pre-pass) and the GEMM quantizing
+// x itself (the same codes, sums and epilogue).
 int run_w8a8(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* w, const float* scale_w, int64_t N,
              const void* bias, void* y, void* buf, hipStream_t s) {
   int8_t* xq = (int8_t*)buf;
   float* sx = (float*)((char*)buf + (((size_t)M * (size_t)K + 255) & ~(size_t)255));
+  if (g_w8a8_fused_quant) {
+    if (int st = hip_status(qlq::launch_row_scales_int8(x, x_dtype, M, K, sx, s), "activation row scales"))
+      return st;
+    return hip_status(qlq::launch_int8_gemm_quant_a(x, x_dtype, w, M, N, K, sx, scale_w, bias, y, s),
+                      "int8 gemm (quantized A)");
+  }
   if (int st = hip_status(qlq::launch_quantize_rows_int8(x, x_dtype, M, K, xq, sx, s), "activation quant"))
     return st;
   return hip_status(qlq::launch_int8_gemm(xq, w, M, N, K, sx, scale_w, bias, x_dtype, y, s), "int8 gemm");

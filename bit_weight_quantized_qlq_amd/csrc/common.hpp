@@ -259,6 +259,22 @@ struct RowDivider {
   }
 };
 
+// The int8 code clamp(rint(d), -128, 127) in the low byte of a word: clamp
+// first (v_med3; the same integer as clamping after rounding), then t +
+// 1.5 * 2^23, which for |t| < 2^22 rounds t to the nearest integer, ties to
+// even as rint does, and leaves it as the two's-complement low bits of the
+// sum's encoding.
+__device__ __forceinline__ uint32_t int8_code_bits(float d) {
+  const float t = __builtin_amdgcn_fmed3f(d, -128.0f, 127.0f);
+  return __float_as_uint(t + 12582912.0f);
+}
+// the low bytes of a, b, c, d as the bytes 0..3 of one word
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // a0, b0, 0, 0
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);  // c0, d0, 0, 0
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);              // a0, b0, c0, d0
+}
+
 // ------------------------------------------------ affine n-bit code streams
 // A row's codes form one LSB-first bit stream (code k at stream bits
 // BITS*k .. BITS*k + BITS - 1, stream bit i = bit i % 32 of word i / 32), so

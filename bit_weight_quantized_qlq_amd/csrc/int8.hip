@@ -95,6 +95,52 @@ __device__ __forceinline__ void store(int8_t* tile, const uint32_t (&bw)[8], int
 }
 }  // namespace w4
 
+// ---- A operand quantized in the kernel (ASRC != 0: a is fp16 / bf16 x and
+// sa its row scales from a pre-pass).  Thread t owns row t / 4 of the
+// 128-row tile and its 64 consecutive k from 64 (t % 4): eight 16-byte loads
+// one tile ahead into registers, then the row quantizer's arithmetic
+// (RowDivider quotient, clamp, round half to even) and four 16-byte chunks of
+// codes into the swizzled A tile, so the codes equal those the standalone
+// quantizer writes.
+namespace qa {
+template <int BK>
+__device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int row, int k0, int K, uint4 (&xa)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = k0 + 8 * i;  // K % 16 == 0: a 16-byte chunk is inside K or past it
+    const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(r, k < K ? (row * K + k) * 2 : kOutOfRange, 0, 0);
+    xa[i] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+template <int ASRC>
+__device__ __forceinline__ float half_to_f32(uint32_t h) {
+  if constexpr (ASRC == 1) return (float)__builtin_bit_cast(f16_t, (uint16_t)h);
+  else return __uint_as_float(h << 16);
+}
+template <int ASRC, int BK, int CPR>
+__device__ __forceinline__ void store(int8_t* tile, const uint4 (&xa)[8], const RowDivider& dv, int row, int cq) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // chunk 4 cq + j: 16 codes from loads 2j and 2j + 1
+    uint32_t w[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 v = xa[2 * j + h];
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+      uint32_t c[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[2 * e] = int8_code_bits(dv.div(half_to_f32<ASRC>(d[e] & 0xFFFFu)));
+        c[2 * e + 1] = int8_code_bits(dv.div(half_to_f32<ASRC>(d[e] >> 16)));
+      }
+      w[2 * h] = pack_low_bytes(c[0], c[1], c[2], c[3]);
+      w[2 * h + 1] = pack_low_bytes(c[4], c[5], c[6], c[7]);
+    }
+    const int c = 4 * cq + j;
+    *reinterpret_cast<u32x4_v*>(tile + row * BK + ((c ^ lds_swz<CPR>(row)) << 4)) = u32x4_v{w[0], w[1], w[2], w[3]};
+  }
+}
+}  // namespace qa
+
 // Pipeline (one barrier per k-iteration).  Before iteration `it`, tiles
 // it .. it+STAGES-2 are in flight to their ring slots.  Iteration it: wait
 // until this thread's loads of tile it have landed, barrier (every thread's
@@ -116,7 +162,11 @@ __device__ __forceinline__ void store(int8_t* tile, const uint32_t (&bw)[8], int
 // BSRC != 0: b is packed int4 [K/2, N] (namespace w4), loaded into registers
 // one tile ahead and written to the B half of the ring slot after the MFMAs
 // of the current tile (BSRC 2: byte loads, for N % 4 != 0).
-template <int OUT, int BK, int STAGES, int PG = 0, int BSRC = 0>
+//
+// ASRC != 0 (1: fp16, 2: bf16): a is the activations x [M, K], quantized to
+// the A tile in the kernel with the row scales sa (namespace qa), the same
+// way: registers one tile ahead, LDS after the current tile's MFMAs.
+template <int OUT, int BK, int STAGES, int PG = 0, int BSRC = 0, int ASRC = 0>
 __global__ void __launch_bounds__(i8::THREADS, 1)
 int8_gemm_kernel(const int8_t* __restrict__ a, const void* __restrict__ b, int M, int N, int K,
                  const float* __restrict__ sa, const float* __restrict__ sb, const void* __restrict__ bias,
@@ -124,6 +174,9 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const void* __restrict__ b, int M
   using namespace i8;
   using C = Cfg<BK, STAGES>;
   constexpr bool W4 = BSRC != 0;
+  constexpr bool QA = ASRC != 0;
+  static_assert(!QA || (!W4 && PG == 0 && OUT != 0 && BK == 256 && STAGES == 2 && THREADS == 512),
+                "quantized A: 128 rows x 256 k, 64 k per thread, double buffer, scaled output");
   static_assert(PG == 0 || (OUT != 0 && PG % KS == 0), "per-group scales need a scaled output");
   static_assert(!W4 || (PG == 0 && OUT != 0 && BK == 256 && STAGES == 2 && THREADS == 512),
                 "int4 B: 128 k-pair rows x 128 columns, 32 bytes per thread, double buffer");
@@ -145,7 +198,8 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const void* __restrict__ b, int M
   const int nk = (K + BK - 1) / BK;
 
   const int rows_a = min(BM, M - m_blk), rows_b = min(BN, N - n_blk);
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(a + (int64_t)m_blk * K, rows_a * K);
+  const __amdgpu_buffer_rsrc_t rsa = QA ? make_rsrc((const uint16_t*)(const void*)a + (int64_t)m_blk * K, rows_a * K * 2)
+                                        : make_rsrc(a + (int64_t)m_blk * K, rows_a * K);
   const int K2 = K / 2;
   const __amdgpu_buffer_rsrc_t rsb =
       W4 ? make_rsrc((const uint8_t*)b + n_blk, K2 * N - n_blk)
@@ -166,7 +220,7 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const void* __restrict__ b, int M
     int8_t* dst_ = smem + ((T) % STAGES) * C::STAGE + wid * ROWS_W * BK;                        \
     _Pragma("unroll") for (int j = 0; j < C::LPW; ++j) {                                        \
       const int o_ = k0_ + kc[j] < K ? voff[j] + k0_ : kOutOfRange;                             \
-      load_lds_b128(rsa, dst_ + 1024 * j, o_);                                                  \
+      if constexpr (!QA) load_lds_b128(rsa, dst_ + 1024 * j, o_);                               \
       if constexpr (!W4) load_lds_b128(rsb, dst_ + C::TILE + 1024 * j, o_);                     \
     }                                                                                           \
   } while (0)
@@ -200,9 +254,16 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const void* __restrict__ b, int M
 
   uint32_t bw[8];  // int4 B: the next tile's packed rows
   if constexpr (W4) w4::load<BSRC == 2>(rsb, 0, K2, N, N - n_blk, rg, cg, bw);
+  // quantized A: this thread's row (t / 4) and 64 k (from 64 (t % 4)), the
+  // row's divisor from its scale
+  const int qa_row = tid >> 2, qa_cq = tid & 3;
+  uint4 xa[8];
+  const RowDivider qa_dv(QA && m_blk + qa_row < M ? sa[m_blk + qa_row] : 1.0f);
+  if constexpr (QA) qa::load<BK>(rsa, qa_row, 64 * qa_cq, K, xa);
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t) QLQ_ISSUE(t);
   if constexpr (W4) w4::store<BK>(smem + C::TILE, bw, rg, cg);
+  if constexpr (QA) qa::store<ASRC, BK, C::CPR>(smem, xa, qa_dv, qa_row, qa_cq);
   if constexpr (PIPE) {
     i32x16_v acc2[2][2];
 #pragma unroll
@@ -278,9 +339,11 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const void* __restrict__ b, int M
         for (int j = 0; j < 2; ++j) scf[f][j] = sb[(int64_t)g * N + ncol[j]];
       }
     }
-    const bool more = W4 && it + 1 < nk;
+    const bool more = (W4 || QA) && it + 1 < nk;
     if constexpr (W4)
       if (more) w4::load<BSRC == 2>(rsb, (it + 1) * (BK / 2), K2, N, N - n_blk, rg, cg, bw);
+    if constexpr (QA)
+      if (more) qa::load<BK>(rsa, qa_row, (it + 1) * BK + 64 * qa_cq, K, xa);
     QLQ_ISSUE(it + STAGES - 1);
     const int8_t* st_ = smem + (it % STAGES) * C::STAGE;
     u32x4_v af[2][C::QN], bf[2][C::QN];
@@ -313,6 +376,8 @@ int8_gemm_kernel(const int8_t* __restrict__ a, const void* __restrict__ b, int M
     }
     if constexpr (W4)
       if (more) w4::store<BK>(smem + ((it + 1) % STAGES) * C::STAGE + C::TILE, bw, rg, cg);
+    if constexpr (QA)
+      if (more) qa::store<ASRC, BK, C::CPR>(smem + ((it + 1) % STAGES) * C::STAGE, xa, qa_dv, qa_row, qa_cq);
   }
 #undef QLQ_ISSUE
   // the zero tiles issued past the end may still be landing in the ring
@@ -457,6 +522,19 @@ hipError_t launch_w4a8_gemm(const int8_t* a, const uint8_t* b, int64_t M, int64_
     if (h) QLQ_W4_LAUNCH(1, 2); else QLQ_W4_LAUNCH(2, 2);
   }
 #undef QLQ_W4_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_int8_gemm_quant_a(const void* x, int x_dtype, const int8_t* b, int64_t M, int64_t N, int64_t K,
+                                    const float* sx, const float* sb, const void* bias, void* out, hipStream_t s) {
+  const int64_t tiles = cdiv(M, i8::BM) * cdiv(N, i8::BN);
+  dim3 grid((unsigned)tiles), block(i8::THREADS);
+  const int m = (int)M, n = (int)N, k = (int)K;
+  const int8_t* a = (const int8_t*)x;  // reinterpreted by the kernel as 16-bit x
+  if (x_dtype == F16)
+    hipLaunchKernelGGL((int8_gemm_kernel<1, 256, 2, 0, 0, 1>), grid, block, 0, s, a, b, m, n, k, sx, sb, bias, out);
+  else
+    hipLaunchKernelGGL((int8_gemm_kernel<2, 256, 2, 0, 0, 2>), grid, block, 0, s, a, b, m, n, k, sx, sb, bias, out);
   return hipGetLastError();
 }
 

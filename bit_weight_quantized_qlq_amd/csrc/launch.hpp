@@ -27,6 +27,8 @@ hipError_t launch_ternary_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* p
 hipError_t launch_quantize_rows_int8(const void* v, int v_dtype, int64_t R, int64_t K,
                                      int8_t* q, float* scale, hipStream_t s, bool nibble_order = false);
 // per-row int8 with the clip at a percentile of |v| (K <= kClipMaxK)
+// the row scales of launch_quantize_rows_int8 alone (K % 16 == 0)
+hipError_t launch_row_scales_int8(const void* v, int v_dtype, int64_t R, int64_t K, float* scale, hipStream_t s);
 constexpr int64_t kClipMaxKHost = 16384;
 hipError_t launch_quantize_rows_int8_clip(const void* v, int v_dtype, int64_t R, int64_t K, float pct, int8_t* q,
                                           float* scale, hipStream_t s);
@@ -52,6 +54,10 @@ hipError_t launch_ternary_forward(const void* x, int x_dtype, int64_t M, int64_t
                                   int invert, const void* bias, void* y, hipStream_t s);
 
 // int8.hip
+// the W8A8 product with the activation quantizer in the GEMM: x [M, K] fp16 /
+// bf16 and its row scales sx (launch_row_scales_int8); out of x's dtype
+hipError_t launch_int8_gemm_quant_a(const void* x, int x_dtype, const int8_t* b, int64_t M, int64_t N, int64_t K,
+                                    const float* sx, const float* sb, const void* bias, void* out, hipStream_t s);
 hipError_t launch_int8_gemm(const int8_t* a, const int8_t* b, int64_t M, int64_t N, int64_t K,
                             const float* sa, const float* sb, const void* bias, int out_dtype,
                             void* out, hipStream_t s);

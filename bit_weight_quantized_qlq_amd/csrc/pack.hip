@@ -321,14 +321,10 @@ quantize_rows_int8_kernel(const T* __restrict__ v, int64_t K, int8_t* __restrict
     uint32_t packed4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t word = 0;
+      uint32_t c[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float r = rintf(dv.div(e[chunk_src<NIB>(4 * i + j)]));
-        r = fminf(fmaxf(r, -128.0f), 127.0f);
-        word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
-      }
-      packed4[i] = word;
+      for (int j = 0; j < 4; ++j) c[j] = int8_code_bits(dv.div(e[chunk_src<NIB>(4 * i + j)]));
+      packed4[i] = pack_low_bytes(c[0], c[1], c[2], c[3]);
     }
     *reinterpret_cast<uint4*>(qr + k) = make_uint4(packed4[0], packed4[1], packed4[2], packed4[3]);
   }
@@ -371,14 +367,10 @@ quantize_rows_int8_wave_kernel(const T* __restrict__ v, int R, int K, int8_t* __
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t word = 0;
+      uint32_t c[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float r = rintf(dv.div(e[g * 16 + chunk_src<NIB>(4 * i + j)]));
-        r = fminf(fmaxf(r, -128.0f), 127.0f);
-        word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
-      }
-      w[i] = word;
+      for (int j = 0; j < 4; ++j) c[j] = int8_code_bits(dv.div(e[g * 16 + chunk_src<NIB>(4 * i + j)]));
+      w[i] = pack_low_bytes(c[0], c[1], c[2], c[3]);
     }
     *reinterpret_cast<uint4*>(q + (int64_t)row * K + (g * 64 + lane) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -424,17 +416,48 @@ quantize_rows_int8_block_kernel(const T* __restrict__ v, int K, int8_t* __restri
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t word = 0;
+      uint32_t c[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float r = rintf(dv.div(e[g * 16 + chunk_src<NIB>(4 * i + j)]));
-        r = fminf(fmaxf(r, -128.0f), 127.0f);
-        word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
-      }
-      w[i] = word;
+      for (int j = 0; j < 4; ++j) c[j] = int8_code_bits(dv.div(e[g * 16 + chunk_src<NIB>(4 * i + j)]));
+      w[i] = pack_low_bytes(c[0], c[1], c[2], c[3]);
     }
     *reinterpret_cast<uint4*>(q + row * K + (g * 256 + tid) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
+}
+
+// The row scales of the row quantizer alone (s = absmax / 127, 1 if 0):
+// one wave per row, four 16-element groups per lane in flight.  The codes
+// are left to the consumer, which divides by these same scales.
+template <typename T>
+__global__ void __launch_bounds__(256)
+row_scales_int8_kernel(const T* __restrict__ v, int R, int K, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const T* vr = v + (int64_t)row * K;
+  float a = 0.0f;
+#pragma unroll 4
+  for (int k = lane * 16; k < K; k += 64 * 16) {  // K % 16 == 0
+    float e[16];
+    load16<T>(vr + k, e);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(e[i]));
+  }
+  a = wave_max_dpp(a);
+  float s = __fdiv_rn(a, 127.0f);
+  if (s == 0.0f) s = 1.0f;
+  if (lane == 0) scale[row] = s;
+}
+
+hipError_t launch_row_scales_int8(const void* v, int v_dtype, int64_t R, int64_t K, float* scale, hipStream_t s) {
+  const dim3 grid((unsigned)cdiv(R, 4)), block(256);
+  const int r = (int)R, k = (int)K;
+  switch (v_dtype) {
+    case F32: hipLaunchKernelGGL(row_scales_int8_kernel<float>, grid, block, 0, s, (const float*)v, r, k, scale); break;
+    case BF16: hipLaunchKernelGGL(row_scales_int8_kernel<bf16_t>, grid, block, 0, s, (const bf16_t*)v, r, k, scale); break;
+    default: hipLaunchKernelGGL(row_scales_int8_kernel<f16_t>, grid, block, 0, s, (const f16_t*)v, r, k, scale); break;
+  }
+  return hipGetLastError();
 }
 
 // Per-group symmetric int8 quantization: w [N, K] -> q [N, K] int8 and
@@ -469,14 +492,10 @@ quantize_groups_int8_kernel(const T* __restrict__ w, int N, int K, int8_t* __res
   uint32_t wd[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t word = 0;
+    uint32_t c[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float r = rintf(dv.div(e[4 * i + j]));
-      r = fminf(fmaxf(r, -128.0f), 127.0f);
-      word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
-    }
-    wd[i] = word;
+    for (int j = 0; j < 4; ++j) c[j] = int8_code_bits(dv.div(e[4 * i + j]));
+    wd[i] = pack_low_bytes(c[0], c[1], c[2], c[3]);
   }
   *reinterpret_cast<uint4*>(q + (int64_t)n * K + k) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
 }

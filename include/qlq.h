@@ -257,6 +257,22 @@ QLQ_API int w8a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * Where the activation quantizer runs ("cider/ops.py", perchannel_linear:
+ * y = dequant(quant_a(x) @ w_int8) + bias).  0 (default): quant_a writes
+ * xq [M, K] int8 and sx [M] to the workspace, then the int8 GEMM reads xq.
+ * 1: a pre-pass writes sx only and the GEMM quantizes each x tile itself
+ * (fp16/bf16 tiles into registers, the same quotient, rounding and clamp, so
+ * the codes, the int32 sums and y are bit-identical to mode 0); every
+ * column block of the GEMM then quantizes its rows again, which costs more
+ * than the xq round trip it saves.  Process-wide, read at each call of
+ * w8a8_linear_forward and w8a8_linear_forward_noalloc; setting it while
+ * another thread launches is a race.  Values other than 0 and 1 are
+ * rejected (QLQ_ERR_INVALID_ARG).
+ */
+QLQ_API int qlq_set_w8a8_fused_quant(int on);
+QLQ_API int qlq_get_w8a8_fused_quant(void);
+
+/*
  * w8a8_linear_forward_noalloc - w8a8_linear_forward for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): the same computation, kernels and

@@ -318,3 +318,12 @@ def test_noalloc_w8a8_validation():
     assert L.w8a8_workspace_size(4093, 4096) > qlq.W8A8_NOALLOC_SCRATCH_BYTES
     assert call(M=4093, K=4096) == qlq.QLQ_ERR_WORKSPACE
     assert "scratch" in qlq.last_error()
+
+
+def test_fused_quant_switch():
+    L = qlq.lib()
+    old = L.qlq_get_w8a8_fused_quant()
+    assert old == 0                                       # the default: quantizer before the GEMM
+    assert L.qlq_set_w8a8_fused_quant(2) == qlq.QLQ_ERR_INVALID_ARG
+    assert L.qlq_set_w8a8_fused_quant(1) == 0 and L.qlq_get_w8a8_fused_quant() == 1
+    assert L.qlq_set_w8a8_fused_quant(0) == 0 and L.qlq_get_w8a8_fused_quant() == 0

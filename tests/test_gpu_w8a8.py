@@ -135,3 +135,69 @@ def test_w8a8_variants(xdt, shape):
     inp = workloads.w8a8_inputs(M, K, N, x_dtype=ODT[xdt], bias=True, seed=M + K + N, outlier_frac=0.01)
     y, y_ref, D = _w8a8_case(inp)
     assert_close(y, y_ref, D, K, xdt, label=f"w8a8 {xdt} {shape}")
+
+
+def _fused_vs_unfused(x, wq, sw, bias=None, noalloc=False):
+    fwd = qlq.w8a8_linear_forward_noalloc if noalloc else qlq.w8a8_linear_forward
+    old = qlq.qlq_get_w8a8_fused_quant()
+    try:
+        qlq.qlq_set_w8a8_fused_quant(0)
+        y0 = fwd(x, wq, sw, bias=bias)
+        qlq.qlq_set_w8a8_fused_quant(1)
+        y1 = fwd(x, wq, sw, bias=bias)
+    finally:
+        qlq.qlq_set_w8a8_fused_quant(old)
+    torch.cuda.synchronize()
+    return y0, y1
+
+
+def test_fused_quant_workload_bit_identical():
+    """The activation quantizer inside the GEMM gives the same codes, sums
+    and epilogue as the quantizer before it: bit-identical outputs on the
+    full workload, and within the tolerance rule of the oracle."""
+    inp = workloads.workload_inputs("w8a8_perchannel")
+    wq_ref, sw_ref = oracle.quantize_rows_int8(inp["w"].numpy())
+    wq, sw = torch.from_numpy(wq_ref).to(dev()), torch.from_numpy(sw_ref).to(dev())
+    y0, y1 = _fused_vs_unfused(inp["x"].to(dev()), wq, sw)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    _, _, _, y_ref, D = oracle.w8a8_forward(f32(inp["x"]), wq_ref, sw_ref)
+    assert_close(y1, y_ref, D, 4096, torch.float16, strict=True, label="w8a8 fused quant workload")
+
+
+@pytest.mark.parametrize("xdt", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(1, 64, 16), (37, 208, 45), (130, 512, 300), (129, 4112, 257), (300, 1040, 128)])
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_fused_quant_ragged_bit_identical(xdt, shape, noalloc):
+    # K tails inside a 256-wide k-iteration, M and N not multiples of 128
+    M, K, N = shape
+    inp = workloads.w8a8_inputs(M, K, N, x_dtype=ODT[xdt], bias=True, seed=M + 3 * K + N, outlier_frac=0.01)
+    wq_ref, sw_ref = oracle.quantize_rows_int8(inp["w"].numpy())
+    wq, sw = torch.from_numpy(wq_ref).to(dev()), torch.from_numpy(sw_ref).to(dev())
+    y0, y1 = _fused_vs_unfused(inp["x"].to(dev()), wq, sw, bias=inp["bias"].to(dev()), noalloc=noalloc)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16)), shape
+    _, _, _, y_ref, D = oracle.w8a8_forward(f32(inp["x"]), wq_ref, sw_ref, bias=f32(inp["bias"]))
+    assert_close(y1, y_ref, D, K, xdt, label=f"w8a8 fused quant {xdt} {shape}")
+
+
+@pytest.mark.parametrize("vdt", [torch.float16, torch.bfloat16])
+def test_fused_quant_every_value(vdt):
+    # every representable value up to a row maximum through the in-GEMM
+    # quantizer, with an identity-like weight that exposes each code: w row n
+    # has a single 1 at k = n, so the int32 sum of output n is x's code at n
+    amax = 3.140625
+    vals = _all_values_up_to(amax, vdt)
+    K = 4096
+    per = K - 1
+    rows = np.zeros(((len(vals) + per - 1) // per, K), dtype=np.float32)
+    rows[:, 0] = amax
+    flat = rows[:, 1:].reshape(-1)
+    flat[: len(vals)] = vals
+    rows[:, 1:] = flat.reshape(rows.shape[0], per)
+    x = torch.from_numpy(rows).to(vdt)
+    xq_ref, sx_ref = oracle.quantize_rows_int8(f32(x))
+    eye = np.zeros((K, K), dtype=np.float32)
+    np.fill_diagonal(eye, 1.0)
+    wq_ref, sw_ref = oracle.quantize_rows_int8(eye)       # 127 on the diagonal, scale 1/127
+    wq, sw = torch.from_numpy(wq_ref).to(dev()), torch.from_numpy(sw_ref).to(dev())
+    y0, y1 = _fused_vs_unfused(x.to(dev()), wq, sw)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
