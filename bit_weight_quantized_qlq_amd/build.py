@@ -89,6 +89,50 @@ def build(verbose=False, extra_flags=None, jobs=None, only=None):
     return LIB
 
 
+# Address and undefined-behaviour sanitizers on the host code only (each
+# -fsanitize directly after -Xarch_host: the device code is built as usual).
+HOST_SANITIZE = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+ABI_DRIVER = os.path.join(ROOT, "tests", "abi_sanitize_driver.cpp")
+
+
+def build_abi_sanitize_driver(verbose=False):
+    """The C ABI's host code (api.cpp) under the address and undefined-behaviour
+    sanitizers, linked with the kernel objects of the last full build and the
+    host-side validation driver (tests/abi_sanitize_driver.cpp) into one
+    executable; returns its path."""
+    sdir = os.path.join(BUILD, "sanitize")
+    os.makedirs(sdir, exist_ok=True)
+    objs = []
+    for src, out in ((os.path.join(CSRC, "api.cpp"), os.path.join(sdir, "api.o")),
+                     (ABI_DRIVER, os.path.join(sdir, "abi_sanitize_driver.o"))):
+        cmd = [HIPCC] + [f for f in CFLAGS if f != "-O3"] + ["-O1", "-g"] + HOST_SANITIZE + \
+              ["-x", "hip", "-c", src, "-o", out]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        objs.append(out)
+    for s in SOURCES[1:]:  # the kernels, as the last full build left them
+        o = os.path.join(BUILD, os.path.splitext(s)[0] + ".o")
+        if not os.path.exists(o):
+            raise RuntimeError(f"{o} is not built: run a full build first")
+        objs.append(o)
+    exe = os.path.join(sdir, "abi_sanitize_driver")
+    cmd = [HIPCC, f"--offload-arch={ARCH}"] + HOST_SANITIZE + ["-o", exe] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    return exe
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")

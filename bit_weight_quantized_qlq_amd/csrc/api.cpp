@@ -345,7 +345,7 @@ QLQ_API int qlq_int8_matmul_int32(const int8_t* a, const int8_t* b, int64_t M, i
 }
 
 QLQ_API size_t w8a8_workspace_size(int64_t M, int64_t K) {
-  if (M <= 0 || K <= 0) return 0;
+  if (M <= 0 || K <= 0 || M >= kMaxDim || K >= kMaxDim) return 0;  // shapes no forward call accepts
   const size_t q = ((size_t)M * (size_t)K + 255) & ~(size_t)255;
   return q + (size_t)M * sizeof(float);
 }
@@ -477,7 +477,7 @@ QLQ_API int qlq_quantize_groups_int8(const void* w, int w_dtype, int64_t N, int6
 }
 
 QLQ_API size_t pergroup_workspace_size(int64_t M, int64_t K) {
-  if (M <= 1 || K <= 0) return 0;  // M == 1 keeps x in floating point
+  if (M <= 1 || K <= 0) return 0;  // M == 1 keeps x in floating point (larger shapes: w8a8_workspace_size gives 0)
   return w8a8_workspace_size(M, K);
 }
 
@@ -532,7 +532,7 @@ QLQ_API int w4a8_pack_weight_int4(const void* w, int w_dtype, int64_t K, int64_t
 }
 
 QLQ_API size_t w4a8_workspace_size(int64_t M, int64_t K, int64_t N) {
-  if (M <= 0 || K <= 0 || N <= 0) return 0;
+  if (M <= 0 || K <= 0 || N <= 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim) return 0;
   const size_t gemm = w8a8_workspace_size(M, K);
   if (M > qlq::kW4a8SkinnyMaxM) return gemm;
   const size_t skinny = qlq::w4a8_skinny_workspace(M, K, N);
