@@ -10,7 +10,10 @@
 // Design (HBM-bound; every weight byte is read exactly once):
 //  * one wave owns R consecutive output rows; its 64 lanes stride over the
 //    row in 16-byte chunks (lane + 64*i), so each load instruction of a wave
-//    covers 1 KiB of contiguous codes;
+//    covers 1 KiB of contiguous codes.  At M == 1 a wave takes one row in
+//    blocks of 16 waves, and with 4-bit codes and N >= QLQ_GEMV_LARGE_N two
+//    rows in blocks of 8 (more bytes in flight per wave, half the block
+//    turnover);
 //  * a chunk never straddles a group (group_size is a multiple of the chunk's
 //    code count), so per chunk and row:  acc += s * P + b * X  with
 //    P = sum x*q and X = sum x;  X is shared by the R rows;
@@ -37,8 +40,13 @@
 #ifndef QLQ_GEMV_R2
 #define QLQ_GEMV_R2 4  // output rows per wave at M == 2
 #endif
+#ifndef QLQ_GEMV_LARGE_N
+#define QLQ_GEMV_LARGE_N 12288  // M == 1, 4-bit codes: from this N on, 2 rows per wave, 8 waves per block
+#endif
 
 namespace qlq {
+
+constexpr int64_t kGemvLargeN = QLQ_GEMV_LARGE_N;
 
 template <typename XT> struct PairTraits;
 template <> struct PairTraits<bf16_t> {
@@ -247,8 +255,8 @@ gemv_pair_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
 // ---------------------------------------------------------------------------
 template <int BITS> constexpr bool kStreamPairs = BITS == 1 || BITS == 3 || BITS == 5 || BITS == 6;
 
-template <int BITS, typename XT, int MT, int R, int NCH, int G>
-__global__ void __launch_bounds__(64 * QLQ_GEMV_WAVES_PER_BLOCK)
+template <int BITS, typename XT, int MT, int R, int NCH, int G, int WPB>
+__global__ void __launch_bounds__(64 * WPB)
 gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t* __restrict__ packed,
                  const XT* __restrict__ scales, const XT* __restrict__ biases, int64_t N,
                  const XT* __restrict__ bias, XT* __restrict__ y) {
@@ -259,7 +267,7 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
   constexpr int XDW = CODES / 2;                     // x dwords per chunk (16)
   constexpr int CPG = G / CODES;                     // chunks per group (1, 2, 4)
   constexpr int NG = NCH >= CPG ? NCH / CPG : 1;     // groups a lane touches
-  constexpr int THREADS = 64 * QLQ_GEMV_WAVES_PER_BLOCK;
+  constexpr int THREADS = 64 * WPB;
   constexpr int XROW = 64 * NCH * 4;                 // 16-byte x units per (padded) row
   constexpr int XU4 = (MT * XROW + THREADS - 1) / THREADS;  // x units staged per thread
   constexpr uint32_t MASK = ((1u << BITS) - 1u) * 0x00010001u;
@@ -273,7 +281,7 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
   __shared__ float xsum[MT][XROW];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = blockIdx.x * QLQ_GEMV_WAVES_PER_BLOCK + __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wave = blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int n0 = wave * R;
   const int m0 = blockIdx.y * MT;
   const int cpr = (int)(K / CODES);
@@ -549,13 +557,16 @@ gemv_generic_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32
 }
 
 // ---------------------------------------------------------------------------
-template <int BITS, typename XT, int MT, int R>
+// FWPB: waves per block of the flat kernel (the other kernels use
+// QLQ_GEMV_WAVES_PER_BLOCK)
+template <int BITS, typename XT, int MT, int R, int FWPB = QLQ_GEMV_WAVES_PER_BLOCK>
 static hipError_t gemv_launch(const void* x, int64_t M, int64_t K, const uint32_t* packed,
                               const void* scales, const void* biases, int64_t N, int G,
                               const void* bias, void* y, hipStream_t s) {
   const int64_t waves = cdiv(N, R);
   dim3 grid((unsigned)cdiv(waves, QLQ_GEMV_WAVES_PER_BLOCK), (unsigned)cdiv(M, MT));
   dim3 block(64 * QLQ_GEMV_WAVES_PER_BLOCK);
+  const dim3 fgrid((unsigned)cdiv(waves, FWPB), (unsigned)cdiv(M, MT)), fblock(64 * FWPB);
   constexpr bool pair = (BITS == 2 || BITS == 4) && !std::is_same<XT, float>::value;
   constexpr bool flat3 = kStreamPairs<BITS> && !std::is_same<XT, float>::value;
   const int64_t nch = cdiv(K / Chunk<BITS>::CODES, kWave);
@@ -563,8 +574,8 @@ static hipError_t gemv_launch(const void* x, int64_t M, int64_t K, const uint32_
     // 1-, 3-, 5-, 6-bit codes: the flat kernel where it applies, else the generic one
     if (MT <= 2 && (nch == 1 || nch == 2 || nch == 4)) {
 #define QLQ_FLAT3(NCH_, G_)                                                                                   \
-  hipLaunchKernelGGL((gemv_flat_kernel<BITS, XT, MT, R, NCH_, G_>), grid, block, 0, s, (const XT*)x, M, K,   \
-                     packed, (const XT*)scales, (const XT*)biases, N, (const XT*)bias, (XT*)y)
+  hipLaunchKernelGGL((gemv_flat_kernel<BITS, XT, MT, R, NCH_, G_, FWPB>), fgrid, fblock, 0, s, (const XT*)x,  \
+                     M, K, packed, (const XT*)scales, (const XT*)biases, N, (const XT*)bias, (XT*)y)
 #define QLQ_FLAT3_G(NCH_)                 \
   do {                                    \
     if (G == 32) QLQ_FLAT3(NCH_, 32);     \
@@ -582,8 +593,8 @@ static hipError_t gemv_launch(const void* x, int64_t M, int64_t K, const uint32_
     }
   } else if constexpr (pair) {
 #define QLQ_FLAT(NCH_, G_)                                                                                    \
-  hipLaunchKernelGGL((gemv_flat_kernel<BITS, XT, MT, R, NCH_, G_>), grid, block, 0, s, (const XT*)x, M, K,   \
-                     packed, (const XT*)scales, (const XT*)biases, N, (const XT*)bias, (XT*)y)
+  hipLaunchKernelGGL((gemv_flat_kernel<BITS, XT, MT, R, NCH_, G_, FWPB>), fgrid, fblock, 0, s, (const XT*)x,  \
+                     M, K, packed, (const XT*)scales, (const XT*)biases, N, (const XT*)bias, (XT*)y)
 #define QLQ_FLAT_G(NCH_)           \
   do {                             \
     if (G == 32) QLQ_FLAT(NCH_, 32);  \
@@ -609,7 +620,13 @@ template <int BITS, typename XT>
 static hipError_t gemv_dispatch_m(const void* x, int64_t M, int64_t K, const uint32_t* packed,
                                   const void* scales, const void* biases, int64_t N, int G,
                                   const void* bias, void* y, hipStream_t s) {
-  if (M == 1) return gemv_launch<BITS, XT, 1, QLQ_GEMV_R1>(x, M, K, packed, scales, biases, N, G, bias, y, s);
+  if (M == 1) {
+    // 4-bit codes and many rows: two rows per wave in blocks of 8 waves keep
+    // more bytes in flight per wave and turn blocks over half as often
+    if (BITS == 4 && N >= kGemvLargeN)
+      return gemv_launch<BITS, XT, 1, 2, 8>(x, M, K, packed, scales, biases, N, G, bias, y, s);
+    return gemv_launch<BITS, XT, 1, QLQ_GEMV_R1>(x, M, K, packed, scales, biases, N, G, bias, y, s);
+  }
   if (M == 2) return gemv_launch<BITS, XT, 2, QLQ_GEMV_R2>(x, M, K, packed, scales, biases, N, G, bias, y, s);
   if (M <= 4) return gemv_launch<BITS, XT, 4, 2>(x, M, K, packed, scales, biases, N, G, bias, y, s);
   return gemv_launch<BITS, XT, 8, 1>(x, M, K, packed, scales, biases, N, G, bias, y, s);

@@ -187,6 +187,24 @@ def test_forward_gemm_tall_blocks_ragged(shape):
     assert_close(y, y_ref, D, K, torch.bfloat16, label=f"gemm tall {shape}")
 
 
+# M == 1 with 4-bit codes and at least 12288 rows: two rows per wave in
+# blocks of 8 waves (flat kernel at one, two and four chunks per lane; the
+# pair kernel at K = 4160; the fp32 generic kernel), N ragged against 16
+LARGE_N_SHAPES = [(1, 512, 12301, 4, 32), (1, 2048, 12303, 4, 64), (1, 4096, 12290, 4, 128),
+                  (1, 4160, 12289, 4, 64), (1, 8192, 12288, 4, 128)]
+
+
+@pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("shape", LARGE_N_SHAPES)
+def test_forward_skinny_large_n(xdt, shape):
+    M, K, N, bits, G = shape
+    if xdt != torch.bfloat16 and K == 8192:
+        pytest.skip("one x dtype at the largest K keeps the oracle's share short")
+    inp = workloads.affine_inputs(M, K, N, x_dtype=ODT[xdt], bias=(N % 2 == 1), seed=K + N)
+    y, y_ref, D = _forward_case(inp, bits, G, xdt)
+    assert_close(y, y_ref, D, K, xdt, label=f"large N {xdt} {shape}")
+
+
 def test_forward_flattens_leading_dims():
     inp = workloads.affine_inputs(6, 256, 48, x_dtype="bf16", bias=True, seed=3)
     x = inp["x"].reshape(2, 3, 256).to(dev())
