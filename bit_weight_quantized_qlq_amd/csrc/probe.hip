@@ -2,12 +2,13 @@
 // that only reads (and does no arithmetic on) the same bytes achieves.
 //
 //  * qlq_probe_read_rows: the byte pattern of the decode GEMV on 4-bit codes
-//    at one x row (one wave per output row, 16 waves per block, each lane
-//    loading its NCH 16-byte code chunks through one buffer descriptor per
-//    row and one 16-bit scale and bias per group it touches, all with the
-//    non-temporal policy, after the block's x loads; x staged in LDS behind
-//    a barrier).  Every loaded word is XOR-folded and one word per row is
-//    stored, so no load can be dropped.
+//    at one x row in the launch shape the GEMV takes for that N (one wave per
+//    output row in blocks of 16 waves; from N = 12288 on, two rows per wave
+//    in blocks of 8), each lane loading its NCH 16-byte code chunks through
+//    one buffer descriptor per row and one 16-bit scale and bias per group it
+//    touches, all with the non-temporal policy, after the block's x loads; x
+//    staged in LDS behind a barrier.  Every loaded word is XOR-folded and one
+//    word per row is stored, so no load can be dropped.
 //  * qlq_probe_read_flat: a plain read of a contiguous buffer, four 16-byte
 //    non-temporal loads per thread, one word stored per block.
 //
@@ -18,7 +19,7 @@
 namespace qlq {
 namespace {
 
-constexpr int kProbeWaves = 16;
+constexpr int64_t kProbeLargeN = 12288;  // the decode GEMV's large-N launch shape from here
 
 __device__ __forceinline__ uint32_t wave_xor(uint32_t v) {
 #pragma unroll
@@ -26,18 +27,18 @@ __device__ __forceinline__ uint32_t wave_xor(uint32_t v) {
   return v;
 }
 
-template <int NCH, int G>
-__global__ void __launch_bounds__(64 * kProbeWaves)
+template <int NCH, int G, int R, int WPB>
+__global__ void __launch_bounds__(64 * WPB)
 read_rows_kernel(const uint16_t* __restrict__ x, int K, const uint32_t* __restrict__ packed,
                  const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, int N,
                  uint32_t* __restrict__ out) {
-  constexpr int THREADS = 64 * kProbeWaves;
+  constexpr int THREADS = 64 * WPB;
   constexpr int XROW = 64 * NCH * 4;                   // 16-byte x units the block stages
   constexpr int XU4 = (XROW + THREADS - 1) / THREADS;
   constexpr int CPG = G / 32;                          // 32-code chunks per group
   __shared__ uint4 xs[XROW];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int n = blockIdx.x * kProbeWaves + __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = (blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(tid >> 6)) * R;
   const int cpr = K / 32, wpr = K / 8, gpr = K / G, kx = K / 8;
 
   uint4 xr[XU4];
@@ -46,20 +47,23 @@ read_rows_kernel(const uint16_t* __restrict__ x, int K, const uint32_t* __restri
     const int u = tid + THREADS * i;
     xr[i] = u < kx ? reinterpret_cast<const uint4*>(x)[u] : make_uint4(0, 0, 0, 0);
   }
-  const int nn = n < N ? n : N - 1;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(packed + (int64_t)nn * wpr, wpr * 4);
-  u32x4_v w[NCH];
-  uint16_t s[NCH], b[NCH];
+  u32x4_v w[R][NCH];
+  uint16_t s[R][NCH], b[R][NCH];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    int c = lane * NCH + i;
-    c = c < cpr ? c : cpr - 1;
-    w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, c * 16, 0, kStreamAux);
-    s[i] = b[i] = 0;
-    const bool first_of_group = NCH >= CPG ? i % CPG == 0 : i == 0;
-    if (first_of_group) {
-      s[i] = stream_load(scales + (int64_t)nn * gpr + c / CPG);
-      b[i] = stream_load(biases + (int64_t)nn * gpr + c / CPG);
+  for (int r = 0; r < R; ++r) {
+    const int nn = n0 + r < N ? n0 + r : N - 1;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(packed + (int64_t)nn * wpr, wpr * 4);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      int c = lane * NCH + i;
+      c = c < cpr ? c : cpr - 1;
+      w[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, c * 16, 0, kStreamAux);
+      s[r][i] = b[r][i] = 0;
+      const bool first_of_group = NCH >= CPG ? i % CPG == 0 : i == 0;
+      if (first_of_group) {
+        s[r][i] = stream_load(scales + (int64_t)nn * gpr + c / CPG);
+        b[r][i] = stream_load(biases + (int64_t)nn * gpr + c / CPG);
+      }
     }
   }
 #pragma unroll
@@ -70,12 +74,15 @@ read_rows_kernel(const uint16_t* __restrict__ x, int K, const uint32_t* __restri
   __syncthreads();
   uint32_t v = 0;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const uint4 xv = xs[(i * 64 + lane) % XROW];
-    v ^= w[i][0] ^ w[i][1] ^ w[i][2] ^ w[i][3] ^ xv.x ^ xv.y ^ xv.z ^ xv.w ^ s[i] ^ ((uint32_t)b[i] << 16);
-  }
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const uint4 xv = xs[(i * 64 + lane) % XROW];
+      v ^= w[r][i][0] ^ w[r][i][1] ^ w[r][i][2] ^ w[r][i][3] ^ xv.x ^ xv.y ^ xv.z ^ xv.w ^ s[r][i] ^
+           ((uint32_t)b[r][i] << 16);
+    }
   v = wave_xor(v);
-  if (lane == 0 && n < N) out[n] = v;
+  if (lane == 0 && n0 < N) out[n0] = v;
 }
 
 constexpr int kFlatThreads = 256, kFlatUnits = 4;
@@ -115,12 +122,21 @@ QLQ_PROBE_API int qlq_probe_read_rows(const void* x, int64_t K, const void* pack
       K / 32 > 256 || N * K >= ((int64_t)1 << 31))
     return -1;
   const int64_t nch = cdiv(K / 32, 64);
-  const dim3 grid((unsigned)cdiv(N, kProbeWaves)), block(64 * kProbeWaves);
+  const bool large = N >= kProbeLargeN;
+  const int R = large ? 2 : 1, WPB = large ? 8 : 16;
+  const dim3 grid((unsigned)cdiv(cdiv(N, R), WPB)), block(64 * WPB);
   hipStream_t s = (hipStream_t)stream;
-#define QLQ_PROBE_ROWS(NCH_, G_)                                                                             \
-  hipLaunchKernelGGL((read_rows_kernel<NCH_, G_>), grid, block, 0, s, (const uint16_t*)x, (int)K,           \
-                     (const uint32_t*)packed, (const uint16_t*)scales, (const uint16_t*)biases, (int)N,      \
-                     (uint32_t*)out)
+#define QLQ_PROBE_ROWS(NCH_, G_)                                                                                 \
+  do {                                                                                                           \
+    if (large)                                                                                                   \
+      hipLaunchKernelGGL((read_rows_kernel<NCH_, G_, 2, 8>), grid, block, 0, s, (const uint16_t*)x, (int)K,      \
+                         (const uint32_t*)packed, (const uint16_t*)scales, (const uint16_t*)biases, (int)N,      \
+                         (uint32_t*)out);                                                                        \
+    else                                                                                                         \
+      hipLaunchKernelGGL((read_rows_kernel<NCH_, G_, 1, 16>), grid, block, 0, s, (const uint16_t*)x, (int)K,     \
+                         (const uint32_t*)packed, (const uint16_t*)scales, (const uint16_t*)biases, (int)N,      \
+                         (uint32_t*)out);                                                                        \
+  } while (0)
 #define QLQ_PROBE_G(NCH_)                                   \
   do {                                                      \
     if (group_size == 32) QLQ_PROBE_ROWS(NCH_, 32);         \
