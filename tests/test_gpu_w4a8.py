@@ -113,8 +113,10 @@ def test_zero_input_gives_bias():
 
 
 @pytest.mark.parametrize("xdt", [torch.float16, torch.bfloat16])
-@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (2, 272, 132), (3, 1040, 517), (4, 128, 260),
-                                   (5, 2048, 384), (8, 16, 4), (7, 784, 1)])
+@pytest.mark.parametrize("M,K,N", [
+    (1, 4096, 4096), (2, 4096, 1024), (1, 8192, 64), (2, 16384, 32), (2, 272, 144), (1, 16, 16),
+    (1, 1040, 4096), (1, 1040, 520), (2, 272, 132), (3, 1040, 517), (4, 128, 260), (5, 2048, 384), (8, 16, 4),
+    (7, 784, 1)])
 def test_skinny_and_gemm_paths_identical(xdt, M, K, N):
     """M <= 8 runs split over K; the GEMM gives the same exact int32 sums and
     the same epilogue, so the two outputs must be bit-identical."""
