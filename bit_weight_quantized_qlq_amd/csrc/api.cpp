@@ -200,7 +200,7 @@ QLQ_API size_t qlq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int bi
                                          int x_dtype) {
   if (M <= 0 || K <= 0 || N <= 0 || group_size <= 0 || K % group_size) return 0;
   if (!takes_gemm(M, K, N, group_size, x_dtype)) return 0;
-  size_t need = (qlq::affine_gemm_workspace(M, K, N, group_size) + 255) & ~(size_t)255;
+  size_t need = (qlq::affine_gemm_workspace(M, K, N, group_size, gemm_bits(bits)) + 255) & ~(size_t)255;
   if (transcoded_gemm(bits)) need += (size_t)N * (size_t)K * gemm_bits(bits) / 8;  // the transcoded codes
   return need;
 }
@@ -236,7 +236,7 @@ QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
     // 8-bit (5, 6: one byte per code) packed layout, and that width's GEMM
     // runs on them with the same scales and biases
     uint32_t* codes = (uint32_t*)((char*)workspace +
-                                  ((qlq::affine_gemm_workspace(M, K, N, group_size) + 255) & ~(size_t)255));
+                                  ((qlq::affine_gemm_workspace(M, K, N, group_size, gemm_bits(bits)) + 255) & ~(size_t)255));
     const int wb = gemm_bits(bits);
     const hipError_t e = wb == 4 ? qlq::launch_affine_to_nibbles(packed, N, K, bits, codes, s)
                                  : qlq::launch_affine_unpack(packed, N, K, bits, (uint8_t*)codes, s);

@@ -31,7 +31,9 @@
 // and the pre-scaled (s', b') pairs go straight from global memory into a
 // ring of LDS stages (one barrier per k-iteration); each wave dequantizes the
 // codes of its own B fragments after reading them from LDS, so codes cross
-// LDS at BITS/16 of the bytes of fp16 weights.  XCD-aware tile order.
+// LDS at BITS/16 of the bytes of fp16 weights.  XCD-aware tile order.  A
+// short tail of tiles past the last whole round of resident blocks runs as
+// k-halves with fp32 partial sums, joined by a small second kernel.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile.hpp"
@@ -265,7 +267,7 @@ __global__ void __launch_bounds__(64 * WV, 8 / WV)
 affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, int M, int K,
                    const uint32_t* __restrict__ packed, const uint32_t* __restrict__ sbt,
                    const int* __restrict__ wexp, int N, int G, const XT* __restrict__ bias,
-                   XT* __restrict__ y) {
+                   XT* __restrict__ y, int tn_full, float* __restrict__ part, int n_split) {
   using namespace gemm;
   using C = Cfg<BITS, BK, STAGES, WV, BMT>;
   constexpr int MI = C::MI;
@@ -277,10 +279,25 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches below
   const int wq = wid & 3, kh = wid >> 2, wm = wq >> 1, wn = wq & 1, h = lane >> 5;
-  int tm, tn;
-  tile_coords<8>(blockIdx.x, (M + BMT - 1) / BMT, (N + BN - 1) / BN, tm, tn);
+  // Blocks below tiles_m * tn_full take whole tiles of columns [0, n_split);
+  // the rest take one k-half of a tile of the last tile columns (block j of
+  // them: half j / tail, tile j % tail) and leave fp32 partial sums
+  int tm, tn, half = -1;
+  const int tiles_m = (M + BMT - 1) / BMT, tiles_n = (N + BN - 1) / BN;
+  const int full = tiles_m * tn_full;
+  int nk = (K + BK - 1) / BK;  // K % 64 == 0; a last half-iteration reads zeros
+  int kb = 0;                  // first k-iteration
+  if ((int)blockIdx.x < full) {
+    tile_coords<8>(blockIdx.x, tiles_m, tn_full, tm, tn);
+  } else {
+    const int j = (int)blockIdx.x - full, tail = tiles_m * (tiles_n - tn_full);
+    half = j / tail;
+    tile_coords<8>(j - half * tail, tiles_m, tiles_n - tn_full, tm, tn);
+    tn += tn_full;
+    nk /= 2;  // K % 128 == 0 on this path
+    kb = half * nk;
+  }
   const int m_blk = tm * BMT, n_blk = tn * BN;
-  const int nk = (K + BK - 1) / BK;  // K % 64 == 0; a last half-iteration reads zeros
   const int rowb = K / PER * 4;      // bytes per packed row
   const int ng = K / G, NP = (N + 3) & ~3;
   const int lg_g = 31 - __builtin_clz(G);  // G is a power of two
@@ -326,7 +343,7 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
 
 #define QLQ_ISSUE(T, SLOT)                                                                        \
   do {                                                                                            \
-    const int k0_ = (T) * BK;                                                                     \
+    const int k0_ = (kb + (T)) * BK;                                                              \
     _Pragma("unroll") for (int j = 0; j < C::APW; ++j)                                            \
         load_lds_b128(rsa, smem + (SLOT) * C::A_TILE + (wid * C::APW + j) * 1024, a_off[j], k0_ * 2); \
     _Pragma("unroll") for (int t = 0; t < OMAX; ++t) {                                            \
@@ -472,6 +489,23 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
         for (int e = 0; e < 16; ++e) acc[i][j][e] += red[(wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane];
   }
 
+  if (half >= 0) {
+    // ---- a k-half of a tail tile: its fp32 sums as they stand (no scaling);
+    // each store instruction writes two rows of 32 consecutive columns
+    float* P = part + (int64_t)half * M * (N - n_split);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m_blk + wm * (BMT / 2) + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int n = n_blk + wn * 64 + 32 * j + (lane & 31);
+          if (m < M && n < N) P[(int64_t)m * (N - n_split) + (n - n_split)] = acc[i][j][e];
+        }
+    return;
+  }
+
   // ---- epilogue: y = 2^(e_m + f_n) * acc + bias, one rounding; each wave
   // stages its rows 64 at a time in its own LDS area and stores them whole
   int fcol[2];
@@ -507,27 +541,72 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
   }
 }
 
-// Workspace: x16 [M, K] fp16 | e_m [M] | f_n [N] | (s', b') [K/G, NP], each
-// part 256-byte aligned.
+// The tail tiles' two k-halves joined: y[m, n] = 2^(e_m + f_n) * (P0 + P1)
+// (+ bias), one rounding, for n in [n_split, N) -- the GEMM epilogue's
+// arithmetic on the sum of the halves.  Four consecutive outputs per thread.
+template <typename XT>
+__global__ void __launch_bounds__(256)
+gemm_tail_join_kernel(const float* __restrict__ part, int M, int N, int n_split, const int* __restrict__ xexp,
+                      const int* __restrict__ wexp, const XT* __restrict__ bias, XT* __restrict__ y) {
+  const int W = N - n_split;
+  const int64_t MW = (int64_t)M * W;
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = i0 + u;
+    if (i >= MW) return;
+    const int m = (int)(i / W), n = n_split + (int)(i - (int64_t)m * W);
+    float t = ldexpf(part[i] + part[MW + i], xexp[m] + wexp[n]);
+    if (bias) t = t + Elem<XT>::load(bias, n);
+    Elem<XT>::store(y, (int64_t)m * N + n, t);
+  }
+}
+
+// Tail split of the tall 4-bit GEMM: 2 * 256 tiles run at once (two blocks
+// per CU), and a tile alone on a CU finishes in about 0.4 of the time a pair
+// sharing it takes.  When the tiles past the last whole paired round are
+// whole tile columns and their k-halves fit one per CU (at most 128 tiles),
+// the halves run as separate blocks and a join kernel adds them; with more
+// tail tiles the halves would share CUs and take longer than the whole tiles.
+struct TailPlan {
+  int tn_full, n_split;
+  bool split;
+  TailPlan(int64_t M, int64_t K, int64_t N, int G, int bits) {
+    const int64_t tiles_m = cdiv(M, gemm::TILE_M_TALL), tiles_n = cdiv(N, gemm::BN);
+    const int64_t T = tiles_m * tiles_n, S = 2 * 256;
+    const int64_t r = T % S;
+    split = bits == 4 && T >= S && r > 0 && 2 * r <= 256 && r % tiles_m == 0 && K % 128 == 0 && (K / 2) % G == 0;
+    tn_full = (int)(split ? tiles_n - r / tiles_m : tiles_n);
+    n_split = split ? tn_full * gemm::BN : (int)N;
+  }
+};
+
+// Workspace: x16 [M, K] fp16 | e_m [M] | f_n [N] | (s', b') [K/G, NP] |
+// with a tail split, the two k-halves' partial sums fp32 [2][M][N - n_split];
+// each part 256-byte aligned.
 struct GemmWs {
-  size_t x16, xe, we, sb, total;
-  GemmWs(int64_t M, int64_t K, int64_t N, int G) {
+  size_t x16, xe, we, sb, pt, total;
+  GemmWs(int64_t M, int64_t K, int64_t N, int G, int bits) {
     const auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const TailPlan tp(M, K, N, G, bits);
     x16 = 0;
     xe = al((size_t)M * (size_t)K * 2);
     we = xe + al((size_t)M * 4);
     sb = we + al((size_t)N * 4);
-    total = sb + (size_t)(K / G) * (size_t)((N + 3) & ~3) * 4;
+    pt = sb + al((size_t)(K / G) * (size_t)((N + 3) & ~3) * 4);
+    total = pt + (tp.split ? (size_t)2 * (size_t)M * (size_t)(N - tp.n_split) * 4 : 0);
   }
 };
 
-size_t affine_gemm_workspace(int64_t M, int64_t K, int64_t N, int G) { return GemmWs(M, K, N, G).total; }
+size_t affine_gemm_workspace(int64_t M, int64_t K, int64_t N, int G, int bits) {
+  return GemmWs(M, K, N, G, bits).total;
+}
 
 template <int BITS, typename XT>
 static hipError_t gemm_launch(const void* x, int64_t M, int64_t K, const uint32_t* packed,
                               const void* scales, const void* biases, int64_t N, int G,
                               const void* bias, void* y, void* ws, hipStream_t s) {
-  const GemmWs L(M, K, N, G);
+  const GemmWs L(M, K, N, G, BITS);
   f16_t* x16 = (f16_t*)((char*)ws + L.x16);
   int* xexp = (int*)((char*)ws + L.xe);
   int* wexp = (int*)((char*)ws + L.we);
@@ -553,12 +632,24 @@ static hipError_t gemm_launch(const void* x, int64_t M, int64_t K, const uint32_
   const int64_t tall_tiles = cdiv(M, gemm::TILE_M_TALL) * cdiv(N, gemm::BN);
   const bool tall = BITS == 4 && tall_tiles >= 2 * 256;
   const int64_t tiles = tall ? tall_tiles : cdiv(M, gemm::TILE_M) * cdiv(N, gemm::BN);
+  const TailPlan tp(M, K, N, G, BITS);  // splits only tall tiles
+  float* part = (float*)((char*)ws + L.pt);
+  const int64_t tail = tp.split ? cdiv(M, gemm::TILE_M_TALL) * (cdiv(N, gemm::BN) - tp.tn_full) : 0;
   auto kern = affine_gemm_kernel<BITS, XT, gemm::KB, gemm::NSTAGES, gemm::WAVES, gemm::TILE_M>;
   if constexpr (BITS == 4)
     if (tall) kern = affine_gemm_kernel<BITS, XT, gemm::KB, gemm::NSTAGES, gemm::WAVES, gemm::TILE_M_TALL>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(64 * gemm::WAVES), 0, s, (const f16_t*)x16,
+  const int tn_full = tp.split ? tp.tn_full : (int)cdiv(N, gemm::BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles + tail)), dim3(64 * gemm::WAVES), 0, s, (const f16_t*)x16,
                      (const int*)xexp, m, k, packed, (const uint32_t*)sbt, (const int*)wexp, n, G,
-                     (const XT*)bias, (XT*)y);
+                     (const XT*)bias, (XT*)y, tn_full, part, tp.n_split);
+  if (tp.split) {
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t outs = M * (N - tp.n_split);
+    hipLaunchKernelGGL(gemm_tail_join_kernel<XT>, dim3((unsigned)cdiv(outs, 1024)), dim3(256), 0, s,
+                       (const float*)part, m, n, tp.n_split, (const int*)xexp, (const int*)wexp,
+                       (const XT*)bias, (XT*)y);
+  }
   return hipGetLastError();
 }
 

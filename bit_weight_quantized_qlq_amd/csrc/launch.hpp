@@ -42,7 +42,8 @@ hipError_t launch_affine_gemv(const void* x, int x_dtype, int64_t M, int64_t K,
                               hipStream_t s);
 
 // gemm.hip: affine prefill GEMM (bf16 / f16 x) on 4- or 8-bit packed codes
-size_t affine_gemm_workspace(int64_t M, int64_t K, int64_t N, int group_size);
+// bits: the width the GEMM runs on (4 or 8)
+size_t affine_gemm_workspace(int64_t M, int64_t K, int64_t N, int group_size, int bits);
 hipError_t launch_affine_gemm(const void* x, int x_dtype, int64_t M, int64_t K,
                               const uint32_t* packed, const void* scales, const void* biases,
                               int64_t N, int bits, int G, const void* bias, void* y,

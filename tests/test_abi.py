@@ -82,11 +82,12 @@ def test_linear_forward_validation(kw, code):
 def test_transcoded_widths_need_room_for_their_codes():
     # 1-, 2- and 3-bit codes are rewritten as nibbles (N*K/2 bytes), 5- and
     # 6-bit codes as bytes (N*K); 4- and 8-bit codes are used as they are
+    # (the 4-bit GEMM's workspace also holds its tail tiles' partial sums)
     L = qlq.lib()
-    base = L.qlq_linear_workspace_size(2048, 4096, 11008, 4, 128, qlq.QLQ_BF16)
-    assert L.qlq_linear_workspace_size(2048, 4096, 11008, 8, 128, qlq.QLQ_BF16) == base
-    for bits, per in ((1, 0.5), (2, 0.5), (3, 0.5), (5, 1), (6, 1)):
-        assert L.qlq_linear_workspace_size(2048, 4096, 11008, bits, 128, qlq.QLQ_BF16) >= base + 11008 * 4096 * per
+    ws = {b: L.qlq_linear_workspace_size(2048, 4096, 11008, b, 128, qlq.QLQ_BF16) for b in (4, 8)}
+    assert 0 < ws[8] <= ws[4]
+    for bits, run, per in ((1, 4, 0.5), (2, 4, 0.5), (3, 4, 0.5), (5, 8, 1), (6, 8, 1)):
+        assert L.qlq_linear_workspace_size(2048, 4096, 11008, bits, 128, qlq.QLQ_BF16) >= ws[run] + 11008 * 4096 * per
     assert L.qlq_linear_workspace_size(4, 4096, 11008, 3, 128, qlq.QLQ_BF16) == 0   # skinny: none
 
 
@@ -327,3 +328,27 @@ def test_fused_quant_switch():
     assert L.qlq_set_w8a8_fused_quant(2) == qlq.QLQ_ERR_INVALID_ARG
     assert L.qlq_set_w8a8_fused_quant(1) == 0 and L.qlq_get_w8a8_fused_quant() == 1
     assert L.qlq_set_w8a8_fused_quant(0) == 0 and L.qlq_get_w8a8_fused_quant() == 0
+
+
+def test_gemm_workspace_holds_tail_partials():
+    """The tall 4-bit GEMM splits the tiles past its last whole paired round
+    over two k-halves when they are whole tile columns and their halves fit
+    one per CU; the workspace then holds the halves' fp32 partial sums."""
+    L = qlq.lib()
+    bf = qlq.QLQ_BF16
+    base = lambda M, K, N, G: M * K * 2 + M * 4 + N * 4 + (K // G) * ((N + 3) // 4 * 4) * 4
+    # 2048 x 9216: 576 tiles = 512 + 8 rows x 8 columns of tail tiles
+    M, K, N, G = 2048, 4096, 9216, 128
+    size = L.qlq_linear_workspace_size(M, K, N, 4, G, bf)
+    assert size >= base(M, K, N, G) + 2 * M * (N - 64 * 128) * 4
+    # 3-bit codes run as 4-bit ones: split, plus the transcoded codes
+    size = L.qlq_linear_workspace_size(M, K, N, 3, G, bf)
+    assert size >= base(M, K, N, G) + 2 * M * (N - 64 * 128) * 4 + N * K // 2
+    # 8-bit codes keep 128-row tiles and never split
+    size = L.qlq_linear_workspace_size(M, K, N, 8, G, bf)
+    assert size < base(M, K, N, G) + 4096
+    # exactly one paired round, or 176 tail tiles (their 352 halves would
+    # share CUs): no split
+    for n in (8192, 11008):
+        size = L.qlq_linear_workspace_size(M, K, n, 4, G, bf)
+        assert base(M, K, n, G) <= size < base(M, K, n, G) + 4096

@@ -171,7 +171,11 @@ def test_forward_paths_ragged(path, xdt, shape):
 # (two blocks per compute unit; 2- and 8-bit codes keep 128-row blocks); M is
 # ragged against 256 and N against 128
 TALL_SHAPES = [(300, 128, 32808, 4, 32), (520, 256, 32808, 4, 128), (300, 192, 32808, 2, 64),
-               (260, 128, 32808, 8, 128), (260, 128, 32808, 3, 32)]
+               (260, 128, 32808, 8, 128), (260, 128, 32808, 3, 32),
+               # the tiles past the last paired round are whole tile columns:
+               # their k-halves run as separate blocks and a join adds them
+               # (ragged M, N ragged inside the tail columns)
+               (1900, 512, 8910, 4, 128), (2048, 384, 8865, 4, 32)]
 
 
 @pytest.mark.parametrize("shape", TALL_SHAPES)
