@@ -209,6 +209,22 @@ def test_forward_skinny_large_n(xdt, shape):
     assert_close(y, y_ref, D, K, xdt, label=f"large N {xdt} {shape}")
 
 
+@pytest.mark.parametrize("xdt", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("bias", [False, True])
+def test_forward_gemm_tail_split_dtypes(xdt, bias):
+    """The split tail's join kernel rounds to either 16-bit dtype, with and
+    without a layer bias, like the GEMM's own epilogue."""
+    M, K, N, bits, G = 1900, 256, 8910, 4, 64
+    inp = workloads.affine_inputs(M, K, N, x_dtype=ODT[xdt], bias=bias, seed=N + int(bias))
+    old = qlq.qlq_get_skinny_max_m()
+    qlq.qlq_set_skinny_max_m(0)
+    try:
+        y, y_ref, D = _forward_case(inp, bits, G, xdt)
+    finally:
+        qlq.qlq_set_skinny_max_m(old)
+    assert_close(y, y_ref, D, K, xdt, label=f"gemm tail split {xdt} bias={bias}")
+
+
 def test_forward_flattens_leading_dims():
     inp = workloads.affine_inputs(6, 256, 48, x_dtype="bf16", bias=True, seed=3)
     x = inp["x"].reshape(2, 3, 256).to(dev())
