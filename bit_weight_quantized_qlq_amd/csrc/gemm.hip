@@ -40,6 +40,10 @@
 
 namespace qlq {
 
+#ifndef QLQ_PREP_ROWS_PER_WAVE
+#define QLQ_PREP_ROWS_PER_WAVE 2  // pre-pass: x rows per wave (their loads all issued first)
+#endif
+
 namespace gemm {
 constexpr int BN = 128;  // block columns
 constexpr int WAVES = 4;     // waves per block (two blocks per compute unit)
@@ -104,13 +108,13 @@ __device__ __forceinline__ void column_block(const XT* __restrict__ scales, cons
   }
 }
 
-// x16[m, k] for one row held by one wave: element k of block b (PER codes)
-// goes to position 2j or 2j+1 of the pair order (j, j + PER/2).  Lanes own
-// groups of 16 consecutive elements, interleaved across the wave (16-byte
-// coalesced loads and stores).  Blocks [0, ceil(N/64)) do the column
-// exponents, whose chains of dependent loads start first that way; the
-// remaining blocks do rows (4 per block).
-template <int BITS, typename XT, int EPT>
+// x16[m, k] for RPW rows held by one wave, one after another: element k of
+// block b (PER codes) goes to position 2j or 2j+1 of the pair order
+// (j, j + PER/2).  Lanes own groups of 16 consecutive elements, interleaved
+// across the wave (16-byte coalesced loads and stores).  Blocks
+// [0, ceil(N/64)) do the column exponents, whose chains of dependent loads
+// start first that way; the remaining blocks do rows (4 waves per block).
+template <int BITS, typename XT, int EPT, int RPW>
 __global__ void __launch_bounds__(256)
 gemm_prep_wave_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ scales,
                       const XT* __restrict__ biases, int N, int G, f16_t* __restrict__ x16,
@@ -124,41 +128,51 @@ gemm_prep_wave_kernel(const XT* __restrict__ x, int M, int K, const XT* __restri
     return;
   }
   const int lane = threadIdx.x & 63;
-  const int m = ((int)blockIdx.x - col_blocks) * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
-  const XT* xr = x + (int64_t)m * K;
-  float e[EPT];
+  const int m0 = (((int)blockIdx.x - col_blocks) * 4 + (threadIdx.x >> 6)) * RPW;
+  if (m0 >= M) return;
+  // every row's loads first: the first row's conversion and stores then
+  // overlap the later rows' reads
+  float e[RPW][EPT];
   bool in[G16];
 #pragma unroll
-  for (int g = 0; g < G16; ++g) {
-    const int k = (g * 64 + lane) * 16;
-    in[g] = k < K;
-    float t[16];
-    load16<XT>(xr + (in[g] ? k : 0), t);
+  for (int r = 0; r < RPW; ++r) {
+    const XT* xr = x + (int64_t)(m0 + r < M ? m0 + r : m0) * K;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) e[g * 16 + i] = in[g] ? t[i] : 0.0f;
-  }
-  float amax = 0.0f;
+    for (int g = 0; g < G16; ++g) {
+      const int k = (g * 64 + lane) * 16;
+      in[g] = k < K;
+      float t[16];
+      load16<XT>(xr + (in[g] ? k : 0), t);
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) amax = fmaxf(amax, fabsf(e[i]));
-  amax = wave_max_dpp(amax);
-  const int ex = amax > 0.0f ? floor_log2(amax) - 14 : 0;
-  if (lane == 0) xexp[m] = ex;
-  f16_t* out = x16 + (int64_t)m * K;
-#pragma unroll
-  for (int g = 0; g < G16; ++g) {
-    if (!in[g]) continue;
-    uint32_t w[8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {  // output pair p = positions 2p, 2p+1 of the 16
-      const int lo = (2 * p) / PER * PER + p % HALF;  // (j, j + PER/2) within block
-      const int i0 = PER >= 16 ? p : lo, i1 = PER >= 16 ? p + HALF : lo + HALF;
-      const f16x2_v h = {(f16_t)ldexpf(e[g * 16 + i0], -ex), (f16_t)ldexpf(e[g * 16 + i1], -ex)};
-      w[p] = __builtin_bit_cast(uint32_t, h);
+      for (int i = 0; i < 16; ++i) e[r][g * 16 + i] = in[g] ? t[i] : 0.0f;
     }
-    uint4* dst = reinterpret_cast<uint4*>(out + (g * 64 + lane) * 16);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int m = m0 + r;
+    if (m >= M) break;
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) amax = fmaxf(amax, fabsf(e[r][i]));
+    amax = wave_max_dpp(amax);
+    const int ex = amax > 0.0f ? floor_log2(amax) - 14 : 0;
+    if (lane == 0) xexp[m] = ex;
+    f16_t* out = x16 + (int64_t)m * K;
+#pragma unroll
+    for (int g = 0; g < G16; ++g) {
+      if (!in[g]) continue;
+      uint32_t w[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {  // output pair p = positions 2p, 2p+1 of the 16
+        const int lo = (2 * p) / PER * PER + p % HALF;  // (j, j + PER/2) within block
+        const int i0 = PER >= 16 ? p : lo, i1 = PER >= 16 ? p + HALF : lo + HALF;
+        const f16x2_v h = {(f16_t)ldexpf(e[r][g * 16 + i0], -ex), (f16_t)ldexpf(e[r][g * 16 + i1], -ex)};
+        w[p] = __builtin_bit_cast(uint32_t, h);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(out + (g * 64 + lane) * 16);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
   }
 }
 
@@ -613,10 +627,11 @@ static hipError_t gemm_launch(const void* x, int64_t M, int64_t K, const uint32_
   uint32_t* sbt = (uint32_t*)((char*)ws + L.sb);
   const int m = (int)M, n = (int)N, k = (int)K;
   if (K <= 64 * 64) {
-    const unsigned blocks = (unsigned)(cdiv(M, 4) + cdiv(N, 64));
+    constexpr int RPW = QLQ_PREP_ROWS_PER_WAVE;
+    const unsigned blocks = (unsigned)(cdiv(M, 4 * RPW) + cdiv(N, 64));
 #define QLQ_PREP(EPT_)                                                                                  \
-  hipLaunchKernelGGL((gemm_prep_wave_kernel<BITS, XT, EPT_>), dim3(blocks), dim3(256), 0, s, (const XT*)x, m, \
-                     k, (const XT*)scales, (const XT*)biases, n, G, x16, xexp, wexp, sbt)
+  hipLaunchKernelGGL((gemm_prep_wave_kernel<BITS, XT, EPT_, RPW>), dim3(blocks), dim3(256), 0, s, (const XT*)x, \
+                     m, k, (const XT*)scales, (const XT*)biases, n, G, x16, xexp, wexp, sbt)
     if (K <= 64 * 16) QLQ_PREP(16);
     else if (K <= 64 * 32) QLQ_PREP(32);
     else QLQ_PREP(64);
