@@ -437,15 +437,20 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
             w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];       \
           }                                                                                        \
         }                                                                                          \
+        const f16x2_v s2 = __builtin_bit_cast(f16x2_v, (ee & 0xFFFFu) * 0x10001u);                 \
+        const f16x2_v b2 = __builtin_bit_cast(f16x2_v, (ee >> 16) * 0x10001u);                     \
+        /* 4-bit: odd nibbles are masked where they sit (16 q 2^-24, still */                       \
+        /* subnormal) and take s' 2^-4: the same product unless s' < 2^-10, */                      \
+        /* i.e. unless a group's scale is 2^24 below its column's largest */                        \
+        const f16x2_v s2h = s2 * (f16x2_v){(f16_t)0.0625f, (f16_t)0.0625f};                        \
         _Pragma("unroll") for (int sl = 0; sl < SPW; ++sl) {                                       \
-          const f16x2_v s2 = __builtin_bit_cast(f16x2_v, (ee & 0xFFFFu) * 0x10001u);               \
-          const f16x2_v b2 = __builtin_bit_cast(f16x2_v, (ee >> 16) * 0x10001u);                   \
           _Pragma("unroll") for (int p = 0; p < 4; ++p) {                                          \
             uint32_t qd;                                                                           \
-            if constexpr (BITS == 4) qd = (w[sl] >> (4 * p)) & MASK;                               \
+            if constexpr (BITS == 4) qd = (p < 2 ? w[sl] : w[sl] >> 8) & (p & 1 ? MASK << 4 : MASK); \
             else qd = (w[2 * sl + (p >> 1)] >> (8 * (p & 1))) & MASK;                              \
             bq[j][sl][p] = __builtin_bit_cast(                                                     \
-                uint32_t, __builtin_elementwise_fma(s2, __builtin_bit_cast(f16x2_v, qd), b2));     \
+                uint32_t, __builtin_elementwise_fma(BITS == 4 && (p & 1) ? s2h : s2,               \
+                                                    __builtin_bit_cast(f16x2_v, qd), b2));         \
           }                                                                                        \
         }                                                                                          \
       }                                                                                            \
