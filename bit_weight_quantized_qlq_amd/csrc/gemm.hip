@@ -437,8 +437,9 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
             w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];       \
           }                                                                                        \
         }                                                                                          \
-        const f16x2_v s2 = __builtin_bit_cast(f16x2_v, (ee & 0xFFFFu) * 0x10001u);                 \
-        const f16x2_v b2 = __builtin_bit_cast(f16x2_v, (ee >> 16) * 0x10001u);                     \
+        const f16x2_v e2 = __builtin_bit_cast(f16x2_v, ee); /* halves: s', b' */                   \
+        const f16x2_v s2 = __builtin_shufflevector(e2, e2, 0, 0);                                  \
+        const f16x2_v b2 = __builtin_shufflevector(e2, e2, 1, 1);                                  \
         /* 4-bit: odd nibbles are masked where they sit (16 q 2^-24, still */                       \
         /* subnormal) and take s' 2^-4: the same product unless s' < 2^-10, */                      \
         /* i.e. unless a group's scale is 2^24 below its column's largest */                        \
