@@ -255,6 +255,21 @@ gemv_pair_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
 // ---------------------------------------------------------------------------
 template <int BITS> constexpr bool kStreamPairs = BITS == 1 || BITS == 3 || BITS == 5 || BITS == 6;
 
+// Pair j = (code j, code j + 16) of a 3-bit unit as two 16-bit lanes.  The
+// two codes lie 48 stream bits apart, so in the words s0, s1, s2 whose halves
+// hold stream bits [16 t, 16 t + 16) and [16 t + 48, 16 t + 64) (byte
+// permutes of the unit's words) both sit at offset 3j mod 16 of their half:
+// one shift and one mask (mask2 = 0x00070007, held in a register) take the
+// pair out.  Pairs 5 and 10 cross a half and take the per-code extraction.
+__device__ __forceinline__ uint32_t unit3_pair(const uint32_t* w, int j, uint32_t mask2) {
+  const int p = 3 * j, t = p >> 4, off = p & 15;
+  if (off + 3 > 16) return unit_code<3>(w, j) | (unit_code<3>(w, j + 16) << 16);
+  const uint32_t sw = t == 0   ? __builtin_amdgcn_perm(w[1], w[0], 0x07060100u)   // w0 lo | w1 hi
+                      : t == 1 ? __builtin_amdgcn_perm(w[2], w[0], 0x05040302u)   // w0 hi | w2 lo
+                               : __builtin_amdgcn_perm(w[2], w[1], 0x07060100u);  // w1 lo | w2 hi
+  return (sw >> off) & mask2;
+}
+
 template <int BITS, typename XT, int MT, int R, int NCH, int G, int WPB>
 __global__ void __launch_bounds__(64 * WPB)
 gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t* __restrict__ packed,
@@ -436,8 +451,9 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
       if constexpr (kStreamPairs<BITS>) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const uint32_t qp =
-              unit_code<BITS>(wv[i][r].w, j) | (unit_code<BITS>(wv[i][r].w, j + 16) << 16) | magic;
+          uint32_t qp;
+          if constexpr (BITS == 3) qp = unit3_pair(wv[i][r].w, j, maskv) | magic;
+          else qp = unit_code<BITS>(wv[i][r].w, j) | (unit_code<BITS>(wv[i][r].w, j + 16) << 16) | magic;
 #pragma unroll
           for (int m = 0; m < MT; ++m) P[m] = PT::dot2(xp[i][m][j], qp, P[m]);
         }
