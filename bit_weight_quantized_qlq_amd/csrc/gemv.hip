@@ -281,12 +281,12 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
   constexpr int PER = kStreamPairs<BITS> ? 1 : 32 / BITS;  // codes per word (2, 4 bits)
   constexpr int XDW = CODES / 2;                     // x dwords per chunk (16)
   constexpr int CPG = G / CODES;                     // chunks per group (1, 2, 4)
-  constexpr int NG = NCH >= CPG ? NCH / CPG : 1;     // groups a lane touches
+  // a lane's chunks c = lane + 64 i lie 64 chunks apart, each in its own group
+  constexpr int NG = NCH;
   constexpr int THREADS = 64 * WPB;
   constexpr int XROW = 64 * NCH * 4;                 // 16-byte x units per (padded) row
   constexpr int XU4 = (MT * XROW + THREADS - 1) / THREADS;  // x units staged per thread
   constexpr uint32_t MASK = ((1u << BITS) - 1u) * 0x00010001u;
-  static_assert(NCH % CPG == 0 || CPG % NCH == 0, "lane span and group must nest");
   static_assert(XDW == 16, "four 16-byte x units per chunk");
 
   // x in code-pair order, laid out [unit q][chunk-in-lane i][lane l] so that
@@ -328,19 +328,16 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
   uint16_t sr[NG][R], br[NG][R];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    int c = lane * NCH + i;
+    int c = i * 64 + lane;  // a load instruction covers 64 consecutive chunks
     c = c < cpr ? c : cpr - 1;  // lanes past the row re-read the last chunk and drop it
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int n = (n0 + r < N) ? n0 + r : (int)N - 1;
       // rows are wave-uniform: one descriptor per row, the lane's chunk in the offset
       wv[i][r] = load_words<WORDS>(make_rsrc(packed + (int64_t)n * wpr, wpr * 4), c * WORDS * 4);
-      if ((NCH >= CPG && i % CPG == 0) || (NCH < CPG && i == 0)) {
-        const int gi = NCH >= CPG ? i / CPG : 0;
-        const int g = c / CPG;
-        sr[gi][r] = stream_load(reinterpret_cast<const uint16_t*>(scales) + (int64_t)n * gpr + g);
-        br[gi][r] = stream_load(reinterpret_cast<const uint16_t*>(biases) + (int64_t)n * gpr + g);
-      }
+      const int g = c / CPG;
+      sr[i][r] = stream_load(reinterpret_cast<const uint16_t*>(scales) + (int64_t)n * gpr + g);
+      br[i][r] = stream_load(reinterpret_cast<const uint16_t*>(biases) + (int64_t)n * gpr + g);
     }
   }
   // ---- 3. stage x: pair order within each word's span, partial sums
@@ -370,7 +367,7 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
       // the staged unit's 8 values (any split of a chunk's 32 works for X)
       const float ps = PT::dot2(p.w, PT::ONES, PT::dot2(p.z, PT::ONES, PT::dot2(p.y, PT::ONES, PT::dot2(p.x, PT::ONES, 0.0f))));
       const int c = u >> 2, q = u & 3;
-      const int pos = q * (64 * NCH) + (c % NCH) * 64 + c / NCH;
+      const int pos = q * (64 * NCH) + c;  // chunk c = lane + 64 i
       xs[m][pos] = p;
       xsum[m][pos] = ps;
     }
@@ -439,8 +436,8 @@ gemv_flat_kernel(const XT* __restrict__ x, int64_t M, int64_t K, const uint32_t*
   constexpr uint32_t magic = PT::MAGIC;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const bool live = lane * NCH + i < cpr;
-    const int gi = NCH >= CPG ? i / CPG : 0;
+    const bool live = i * 64 + lane < cpr;
+    const int gi = i;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float s = bits16_to_f32<XT>(sr[gi][r]), b = bits16_to_f32<XT>(br[gi][r]);

@@ -4,9 +4,10 @@
 //  * qlq_probe_read_rows: the byte pattern of the decode GEMV on 4-bit codes
 //    at one x row in the launch shape the GEMV takes for that N (one wave per
 //    output row in blocks of 16 waves; from N = 12288 on, two rows per wave
-//    in blocks of 8), each lane loading its NCH 16-byte code chunks through
-//    one buffer descriptor per row and one 16-bit scale and bias per group it
-//    touches, all with the non-temporal policy, after the block's x loads; x
+//    in blocks of 8), each lane loading its NCH 16-byte code chunks (chunk
+//    lane + 64 i, so a load instruction covers 1 KiB of contiguous codes)
+//    through one buffer descriptor per row and the 16-bit scale and bias of
+//    each chunk's group, all with the non-temporal policy, after the block's x loads; x
 //    staged in LDS behind a barrier.  Every loaded word is XOR-folded and one
 //    word per row is stored, so no load can be dropped.
 //  * qlq_probe_read_flat: a plain read of a contiguous buffer, four 16-byte
@@ -55,15 +56,11 @@ read_rows_kernel(const uint16_t* __restrict__ x, int K, const uint32_t* __restri
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(packed + (int64_t)nn * wpr, wpr * 4);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      int c = lane * NCH + i;
+      int c = i * 64 + lane;  // the GEMV's chunks: lane + 64 i, each in its own group
       c = c < cpr ? c : cpr - 1;
       w[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, c * 16, 0, kStreamAux);
-      s[r][i] = b[r][i] = 0;
-      const bool first_of_group = NCH >= CPG ? i % CPG == 0 : i == 0;
-      if (first_of_group) {
-        s[r][i] = stream_load(scales + (int64_t)nn * gpr + c / CPG);
-        b[r][i] = stream_load(biases + (int64_t)nn * gpr + c / CPG);
-      }
+      s[r][i] = stream_load(scales + (int64_t)nn * gpr + c / CPG);
+      b[r][i] = stream_load(biases + (int64_t)nn * gpr + c / CPG);
     }
   }
 #pragma unroll
