@@ -147,6 +147,10 @@ SHAPES = [  # (M, K, N, bits, G)
     # code-stream pairs (j, j+16) at 5, 6 and 1 bits
     (2, 640, 77, 5, 64), (1, 448, 130, 6, 64), (2, 384, 129, 1, 128), (1, 4096, 96, 6, 128),
     (2, 8192, 40, 5, 32), (1, 2048, 33, 3, 64),
+    # the flat kernel's lane l takes chunks l + 64 i, each with its own
+    # group's scale and bias: group_size 128 (four chunks a group), and K
+    # with four chunks per lane and a ragged last one
+    (1, 4096, 100, 4, 128), (2, 4224, 70, 4, 128), (1, 4224, 64, 3, 128), (2, 6144, 40, 4, 32),
 ]
 
 
