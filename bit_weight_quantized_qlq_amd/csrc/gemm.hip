@@ -216,11 +216,10 @@ gemm_prep_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ 
 }
 
 // ------------------------------------------------------------------- GEMM
-// Block: WV waves, tile 128x128.  Wave (wq, kh) owns the 64x64 sub-tile wq
-// and, with 8 waves, half kh of every k-iteration's k-steps (the halves are
-// summed through LDS at the end); with 4 waves every wave takes all k-steps
-// and two blocks share a compute unit.  Per stage of the LDS ring:
-//   A  : 128 rows of x16, BK values (2*BK bytes) each, 16-byte chunks swizzled
+// Block: 4 waves, tile BMT x 128 (BMT = 128 or 256).  Wave (wm, wn) owns the
+// (BMT/2) x 64 sub-tile (wm, wn) and takes every k-step; two blocks share a
+// compute unit.  Per stage of the LDS ring:
+//   A  : BMT rows of x16, BK values (2*BK bytes) each, 16-byte chunks swizzled
 //   B  : 128 packed rows, RB = BK*BITS/8 bytes each, chunks swizzled
 //   SB : per 64-k sub-block, 512 bytes per group it touches: (s', b') of the
 //        block's 128 columns
@@ -238,9 +237,8 @@ gemm_prep_kernel(const XT* __restrict__ x, int M, int K, const XT* __restrict__ 
 namespace gemm {
 template <int BITS, int BK, int STAGES, int WV, int BMT> struct Cfg {
   static_assert(BITS == 4 || BITS == 8, "4- or 8-bit packed codes");
-  static constexpr int KSPLIT = WV / 4;             // waves per sub-tile (k-split)
   static constexpr int MI = BMT / 64;               // MFMA row tiles per wave (wave tile BMT/2 x 64)
-  static constexpr int SPW = 4 / KSPLIT;            // k-steps per wave per 64-k sub-block
+  static constexpr int SPW = 4;                     // k-steps per 64-k sub-block
   static constexpr int U = BK / 64;                 // 64-k sub-blocks per k-iteration
   static constexpr int A_ROW = 2 * BK;              // bytes per A row
   static constexpr int A_CB = A_ROW / 16;           // chunks per A row
@@ -261,13 +259,13 @@ template <int BITS, int BK, int STAGES, int WV, int BMT> struct Cfg {
   static constexpr int APW = A_LOADS / WV;          // A loads per wave
   static constexpr int NO = B_LOADS + U;            // B and SB loads, dealt round-robin
   static constexpr int LW = APW + NO / WV;          // loads per wave per stage (waves < NO % WV: +1)
-  static constexpr int LDS = STAGES * STAGE > 4 * 64 * 64 * 4 || KSPLIT == 1 ? STAGES * STAGE : 4 * 64 * 64 * 4;
-  static_assert(WV == 4 || WV == 8, "waves");
-  static_assert(BMT % 64 == 0 && BMT <= 256 && (KSPLIT == 1 || BMT == 128), "block rows");
+  static constexpr int LDS = STAGES * STAGE;
+  static_assert(WV == 4, "waves: a 2 x 2 grid of wave tiles");
+  static_assert(BMT % 64 == 0 && BMT <= 256, "block rows");
   static_assert(A_LOADS % WV == 0 && B_TILE % 1024 == 0, "tile split");
   static_assert(STAGES == 2, "double buffer: every wait drains this wave's loads");
   static_assert(BK == 64, "K % 64 == 0 on this path: no k-iteration crosses K");
-  static_assert(LDS * (KSPLIT == 1 ? 2 : 1) <= 160 * 1024, "LDS");
+  static_assert(2 * LDS <= 160 * 1024, "LDS: two blocks per compute unit");
 };
 }  // namespace gemm
 
@@ -292,7 +290,7 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches below
-  const int wq = wid & 3, kh = wid >> 2, wm = wq >> 1, wn = wq & 1, h = lane >> 5;
+  const int wm = wid >> 1, wn = wid & 1, h = lane >> 5;
   // Blocks below tiles_m * tn_full take whole tiles of columns [0, n_split);
   // the rest take one k-half of a tile of the last tile columns (block j of
   // them: half j / tail, tile j % tail) and leave fp32 partial sums
@@ -373,7 +371,7 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
   } while (0)
 
   // ---- fragment addresses in slot 0 (slot s adds s times a tile).  This
-  // wave's k-steps of a sub-block are s = kh*SPW + sl, sl < SPW.
+  // wave takes every k-step s < SPW of a sub-block.
   // B: the words of those steps are contiguous: NBW words from byte boff
   constexpr int NBW = BITS == 8 ? 2 * SPW : SPW;
   constexpr int NBR = NBW == 8 ? 2 : 1;  // 16-byte B reads per fragment
@@ -387,7 +385,7 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
     for (int u = 0; u < C::U; ++u)
 #pragma unroll
       for (int sl = 0; sl < SPW; ++sl) {
-        const int st = kh * SPW + sl;
+        const int st = sl;
         const int c = 8 * u + 4 * h + st;
         aoff[i][u][sl] = ra * C::A_ROW + (c ^ lds_swz<C::A_CB>(ra)) * 16;
       }
@@ -398,7 +396,7 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
 #pragma unroll
     for (int u = 0; u < C::U; ++u) {
       // first word of this wave's steps within the row's sub-block
-      const int w0 = BITS == 4 ? 4 * h + kh * SPW : 8 * h + 2 * kh * SPW;
+      const int w0 = BITS == 4 ? 4 * h : 8 * h;
       const int cb = (C::RB / C::U / 16) * u + w0 / 4;  // chunk (4 words per chunk)
 #pragma unroll
       for (int q = 0; q < NBR; ++q)
@@ -486,29 +484,6 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
 #undef QLQ_ISSUE
 #undef QLQ_COMPUTE
 
-  if constexpr (C::KSPLIT == 2) {
-    // ---- join the two k-halves: waves 4-7 park their sums in LDS, waves
-    // 0-3 add them and run the epilogue
-    float* red = reinterpret_cast<float*>(smem);  // 4 sub-tiles x 64 values x 64 lanes
-    __syncthreads();
-    if (kh == 1) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) red[(wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane] = acc[i][j][e];
-    }
-    __syncthreads();
-    if (kh == 1) return;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] += red[(wq * 64 + (i * 2 + j) * 16 + e) * 64 + lane];
-  }
-
   if (half >= 0) {
     // ---- a k-half of a tail tile: its fp32 sums as they stand (no scaling);
     // each store instruction writes two rows of 32 consecutive columns
@@ -536,9 +511,9 @@ affine_gemm_kernel(const f16_t* __restrict__ x16, const int* __restrict__ xexp, 
     fcol[j] = wexp[n];
     bcol[j] = bias ? Elem<XT>::load(bias, n) : 0.0f;
   }
-  static_assert(C::KSPLIT == 2 ? kTileStageBytes <= 64 * 64 * 4 : 4 * kTileStageBytes <= C::LDS, "staging fits");
-  if constexpr (C::KSPLIT == 1) __syncthreads();  // every wave is done with the ring
-  int8_t* stage = smem + (C::KSPLIT == 2 ? wq * 64 * 64 * 4 : wid * kTileStageBytes);
+  static_assert(4 * kTileStageBytes <= C::LDS, "staging fits");
+  __syncthreads();  // every wave is done with the ring
+  int8_t* stage = smem + wid * kTileStageBytes;
   const int col0 = n_blk + wn * 64;
 #pragma unroll
   for (int hf = 0; hf < MI / 2; ++hf) {
