@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -15,8 +16,10 @@
 namespace {
 
 thread_local std::string g_err;
-int g_skinny_max_m = 8;
-int g_w8a8_fused_quant = 0;  // W8A8: activation quantizer inside the GEMM (1) or before it (0)
+// process-wide switches; each call reads a switch once, so a call that
+// overlaps a change takes one setting or the other throughout
+std::atomic<int> g_skinny_max_m{8};
+std::atomic<int> g_w8a8_fused_quant{0};  // W8A8: activation quantizer inside the GEMM (1) or before it (0)
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -104,8 +107,8 @@ int check_affine_shape(int64_t N, int64_t K, int bits, int G) {
 // and the (s', b') table (4 (K/G) N bytes) must stay below 2^31 bytes; other
 // shapes take the skinny kernel.
 constexpr int64_t kGemmTallestTileRows = 256;
-bool takes_gemm(int64_t M, int64_t K, int64_t N, int G, int x_dtype) {
-  return x_dtype != QLQ_F32 && M > g_skinny_max_m && K % 64 == 0 && K * 2 * kGemmTallestTileRows < kMaxDim &&
+bool takes_gemm(int64_t M, int64_t K, int64_t N, int G, int x_dtype, int skinny_max_m) {
+  return x_dtype != QLQ_F32 && M > skinny_max_m && K % 64 == 0 && K * 2 * kGemmTallestTileRows < kMaxDim &&
          (K / G) * ((N + 3) & ~(int64_t)3) * 4 < kMaxDim;
 }
 
@@ -131,17 +134,17 @@ QLQ_API int qlq_device_check(int device) {
 
 QLQ_API int qlq_set_skinny_max_m(int m) {
   QLQ_REQUIRE(m >= 0, QLQ_ERR_INVALID_ARG, "skinny max M must be >= 0 (got %d)", m);
-  g_skinny_max_m = m;
+  g_skinny_max_m.store(m, std::memory_order_relaxed);
   return ok();
 }
-QLQ_API int qlq_get_skinny_max_m(void) { return g_skinny_max_m; }
+QLQ_API int qlq_get_skinny_max_m(void) { return g_skinny_max_m.load(std::memory_order_relaxed); }
 
 QLQ_API int qlq_set_w8a8_fused_quant(int on) {
   QLQ_REQUIRE(on == 0 || on == 1, QLQ_ERR_INVALID_ARG, "fused activation quant must be 0 or 1 (got %d)", on);
-  g_w8a8_fused_quant = on;
+  g_w8a8_fused_quant.store(on, std::memory_order_relaxed);
   return ok();
 }
-QLQ_API int qlq_get_w8a8_fused_quant(void) { return g_w8a8_fused_quant; }
+QLQ_API int qlq_get_w8a8_fused_quant(void) { return g_w8a8_fused_quant.load(std::memory_order_relaxed); }
 
 // ----------------------------------------------------------------- affine
 QLQ_API int qlq_pack(const float* w, int64_t N, int64_t K, int bits, int group_size, uint32_t* packed,
@@ -196,13 +199,21 @@ QLQ_API int qlq_dequantize(const uint32_t* packed, const void* scales, const voi
                     "dequantize");
 }
 
+namespace {
+// workspace of the GEMM path: pre-pass outputs and partials, then the
+// transcoded codes for 1-, 2-, 3-, 5- and 6-bit codes
+size_t affine_gemm_ws_bytes(int64_t M, int64_t K, int64_t N, int bits, int G) {
+  size_t need = (qlq::affine_gemm_workspace(M, K, N, G, gemm_bits(bits)) + 255) & ~(size_t)255;
+  if (transcoded_gemm(bits)) need += (size_t)N * (size_t)K * gemm_bits(bits) / 8;
+  return need;
+}
+}  // namespace
+
 QLQ_API size_t qlq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int bits, int group_size,
                                          int x_dtype) {
   if (M <= 0 || K <= 0 || N <= 0 || group_size <= 0 || K % group_size) return 0;
-  if (!takes_gemm(M, K, N, group_size, x_dtype)) return 0;
-  size_t need = (qlq::affine_gemm_workspace(M, K, N, group_size, gemm_bits(bits)) + 255) & ~(size_t)255;
-  if (transcoded_gemm(bits)) need += (size_t)N * (size_t)K * gemm_bits(bits) / 8;  // the transcoded codes
-  return need;
+  if (!takes_gemm(M, K, N, group_size, x_dtype, g_skinny_max_m.load(std::memory_order_relaxed))) return 0;
+  return affine_gemm_ws_bytes(M, K, N, bits, group_size);
 }
 
 QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* packed,
@@ -219,9 +230,10 @@ QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
   QLQ_REQUIRE(aligned(x, 16) && aligned(packed, 16), QLQ_ERR_ALIGNMENT, "x / packed not 16-byte aligned");
   QLQ_REQUIRE(aligned(scales, es) && aligned(biases, es) && aligned(y, es) && (!bias || aligned(bias, es)),
               QLQ_ERR_ALIGNMENT, "misaligned scales / biases / bias / y");
-  const bool gemm = takes_gemm(M, K, N, group_size, x_dtype);
+  // one read of the threshold decides the path and the workspace it needs
+  const bool gemm = takes_gemm(M, K, N, group_size, x_dtype, g_skinny_max_m.load(std::memory_order_relaxed));
   if (gemm) {
-    const size_t need = qlq_linear_workspace_size(M, K, N, bits, group_size, x_dtype);
+    const size_t need = affine_gemm_ws_bytes(M, K, N, bits, group_size);
     QLQ_REQUIRE(workspace && workspace_bytes >= need, QLQ_ERR_WORKSPACE,
                 "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
     QLQ_REQUIRE(aligned(workspace, 256), QLQ_ERR_ALIGNMENT, "workspace not 256-byte aligned");
@@ -378,7 +390,7 @@ int run_w8a8(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* w, 
              const void* bias, void* y, void* buf, hipStream_t s) {
   int8_t* xq = (int8_t*)buf;
   float* sx = (float*)((char*)buf + (((size_t)M * (size_t)K + 255) & ~(size_t)255));
-  if (g_w8a8_fused_quant) {
+  if (g_w8a8_fused_quant.load(std::memory_order_relaxed)) {
     if (int st = hip_status(qlq::launch_row_scales_int8(x, x_dtype, M, K, sx, s), "activation row scales"))
       return st;
     return hip_status(qlq::launch_int8_gemm_quant_a(x, x_dtype, w, M, N, K, sx, scale_w, bias, y, s),
@@ -560,7 +572,7 @@ QLQ_API int w4a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K
   QLQ_REQUIRE(aligned(workspace, 16), QLQ_ERR_ALIGNMENT, "workspace not 16-byte aligned");
   if (int st = current_device_status()) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (M <= qlq::kW4a8SkinnyMaxM && M <= g_skinny_max_m)
+  if (M <= qlq::kW4a8SkinnyMaxM && M <= g_skinny_max_m.load(std::memory_order_relaxed))
     return hip_status(qlq::launch_w4a8_skinny(x, x_dtype, M, K, packed_w, N, scale_w, bias, y, workspace, s),
                       "w4a8 skinny");
   int8_t* xq = (int8_t*)workspace;

@@ -163,8 +163,10 @@ QLQ_API int qlq_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K,
 
 /*
  * Dispatch threshold: calls with M <= this value take the skinny kernel.
- * Process-wide; setting it while another thread launches is a race.  Values
- * < 0 are rejected.  Used by the tests to force either path.
+ * Process-wide.  A call reads it once, so a call that overlaps a change takes
+ * one path, with the workspace that path needs, and
+ * qlq_linear_workspace_size answers for the value it reads.  Values < 0 are
+ * rejected.  Used by the tests to force either path.
  */
 QLQ_API int qlq_set_skinny_max_m(int m);
 QLQ_API int qlq_get_skinny_max_m(void);
@@ -264,10 +266,10 @@ QLQ_API int w8a8_linear_forward(const void* x, int x_dtype, int64_t M, int64_t K
  * (fp16/bf16 tiles into registers, the same quotient, rounding and clamp, so
  * the codes, the int32 sums and y are bit-identical to mode 0); every
  * column block of the GEMM then quantizes its rows again, which costs more
- * than the xq round trip it saves.  Process-wide, read at each call of
- * w8a8_linear_forward and w8a8_linear_forward_noalloc; setting it while
- * another thread launches is a race.  Values other than 0 and 1 are
- * rejected (QLQ_ERR_INVALID_ARG).
+ * than the xq round trip it saves.  Process-wide, read once at each call of
+ * w8a8_linear_forward and w8a8_linear_forward_noalloc (both modes use the
+ * same workspace), so a call that overlaps a change runs one mode or the
+ * other.  Values other than 0 and 1 are rejected (QLQ_ERR_INVALID_ARG).
  */
 QLQ_API int qlq_set_w8a8_fused_quant(int on);
 QLQ_API int qlq_get_w8a8_fused_quant(void);
